@@ -1,0 +1,30 @@
+"""Reference oracle for chunk-causal rolling-window attention (TEST INFRASTRUCTURE).
+
+Plain, slow, float64 numpy code that states what the streaming attention
+path computes, so that the HIP library can be checked against it.  Only the
+tests, the smoke check and the benchmark's CPU-baseline leg may import this
+package; the product path never calls it and shares no code with it.
+
+Contents
+  window.py     the streaming window as a plain list of frames (anchor frames
+                plus the newest W frames) and the equivalent full-sequence
+                sliding-window mask.
+  attention.py  softmax(Q K^T / sqrt(d)) V in float64 over a key set, with the
+                optional 128x128 block mask and grouped-query heads.
+
+Every function is pinned by tests in tests/test_oracle_pins.py (closed forms,
+invariants, the window tables derived from the pages, and PyTorch's
+scaled_dot_product_attention in float64 on small cases).  Parity unpinned:
+none.
+"""
+from .window import FrameListWindow, sliding_window_allowed, visible_frames_after
+from .attention import attend, attend_full_sequence, executed_pairs
+
+__all__ = [
+    "FrameListWindow",
+    "sliding_window_allowed",
+    "visible_frames_after",
+    "attend",
+    "attend_full_sequence",
+    "executed_pairs",
+]
