@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark of the streaming attention path on one MI355X.
+
+One step = one streaming step of the workload at steady state: append the
+step's F new frames of K/V to the rolling cache (uf_kvcache_append) and run
+chunk attention of the step's queries over the visible window, with the
+step's seeded 128x128 block mask (uf_attn_step).  Inputs (q, k, v, masks)
+are resident in HBM before the timed region starts.
+
+Prints one JSON line.  `value` is executed attention TFLOP/s over the whole
+step (append included); `roofline` rates the attention kernel alone from HIP
+events on the launch stream; `cpu_baseline` times the float64 oracle on a
+bounded sample of the same step on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from synth import CONFIGS, TILE, bf16_bits_to_f32, draw_step_tensors, make_block_mask  # noqa: E402
+
+METRIC = "attention TFLOP/s (% bf16 MFMA peak) + frames/s at 1K and 2K chunk shapes"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 FLOP/clk/CU)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def executed_flops(n_q, n_k, n_q_heads, d, mask):
+    """4*d per (query, key, head) score entry actually computed (kept tiles, valid rows/cols)."""
+    if mask is None:
+        return 4 * d * n_q * n_k * n_q_heads
+    bm = mask != 0
+    rows = np.minimum(TILE, n_q - TILE * np.arange(bm.shape[1]))
+    cols = np.minimum(TILE, n_k - TILE * np.arange(bm.shape[2]))
+    pairs = int((bm * rows[None, :, None] * cols[None, None, :]).sum())
+    if bm.shape[0] == 1:
+        pairs *= n_q_heads
+    return 4 * d * pairs
+
+
+def to_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def steady_keys(cfg):
+    """Visible keys once the window is full."""
+    return (cfg.anchor_frames + cfg.window_frames) * cfg.tokens_per_frame
+
+
+def prepare(cfg, n_steps):
+    """Device inputs of the stream's first n_steps steps (bf16 q/k/v, uint8 masks)."""
+    import torch
+    pool = []
+    for s in range(n_steps):
+        qb, kb, vb = draw_step_tensors(cfg, s)
+        item = {"q": to_dev(qb), "k": to_dev(kb), "v": to_dev(vb), "mask": None, "mask_np": None}
+        pool.append(item)
+    return pool
+
+
+def attach_masks(cfg, pool, n_keys_per_step):
+    import torch
+    for s, item in enumerate(pool):
+        if cfg.mask_pct is not None:
+            m = make_block_mask(cfg.index, s, cfg.n_q_heads, cfg.q_tokens, n_keys_per_step[s], cfg.mask_pct)
+            item["mask_np"] = m
+            item["mask"] = torch.from_numpy(m).to("cuda:0")
+
+
+def run_workload(cfg, warmup, steps):
+    import torch
+    from windowed_attention_amd import KVCache
+
+    F, L = cfg.frames_per_step, cfg.tokens_per_frame
+    # the stream's first steps fill the window; later steps reuse the pool's steady-state inputs
+    fill = -(-(cfg.anchor_frames + cfg.window_frames) // F)
+    n_pool = max(cfg.steps if cfg.steps <= 8 else fill + 2, fill + 1)
+    t0 = time.time()
+    pool = prepare(cfg, n_pool)
+    cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, cfg.window_frames, cfg.anchor_frames)
+    # key counts per pool step follow the window bookkeeping of the library itself
+    n_keys = []
+    for s in range(n_pool):
+        plan = cache.plan_append(F)
+        n_keys.append(plan.window_after.n_keys)
+        cache.append(None, None, F, flags=2)  # UF_APPEND_COMMIT_ONLY: bookkeeping only, nothing copied
+    cache.reset()
+    attach_masks(cfg, pool, n_keys)
+    prep_s = time.time() - t0
+
+    out = torch.empty_like(pool[0]["q"])
+    steady = list(range(fill, n_pool)) or [n_pool - 1]
+
+    def one_step(item, ev=None):
+        if ev is not None:
+            ev[0].record()
+        cache.append(item["k"], item["v"], F)
+        if ev is not None:
+            ev[1].record()
+        cache.attn_step(item["q"], out, item["mask"])
+        if ev is not None:
+            ev[2].record()
+
+    # warm-up: the stream's opening steps (window filling), then steady steps
+    for s in range(n_pool):
+        one_step(pool[s])
+    for i in range(max(0, warmup - n_pool)):
+        one_step(pool[steady[i % len(steady)]])
+    torch.cuda.synchronize()
+    assert cache.window().n_keys == steady_keys(cfg)
+
+    seq = [steady[i % len(steady)] for i in range(steps)]
+    flops = [executed_flops(cfg.q_tokens, steady_keys(cfg), cfg.n_q_heads, cfg.head_dim, pool[s]["mask_np"])
+             for s in seq]
+    # timed region: wall clock over exactly `steps` steps
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in seq:
+        one_step(pool[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    # per-kernel durations from HIP events on the launch stream (separate pass, same steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in seq]
+    torch.cuda.synchronize()
+    for s, ev in zip(seq, evs):
+        one_step(pool[s], ev)
+    torch.cuda.synchronize()
+    append_ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evs]))
+    attn_ms = float(np.mean([ev[1].elapsed_time(ev[2]) for ev in evs]))
+    cache.close()
+
+    total_flops = float(sum(flops))
+    append_bytes = 4 * F * L * cfg.n_kv_heads * cfg.head_dim * 2  # K and V, each read and written
+    ms_per_step = 1e3 * wall / steps
+    return {
+        "cfg": cfg,
+        "prep_s": prep_s,
+        "ms_per_step": ms_per_step,
+        "tflops": total_flops / wall / 1e12,
+        "frames_per_s": F * steps / wall,
+        "attn_ms": attn_ms,
+        "append_ms": append_ms,
+        "attn_tflops": (total_flops / steps) / (attn_ms * 1e-3) / 1e12,
+        "flops_per_step": total_flops / steps,
+        "append_gbs": append_bytes / (append_ms * 1e-3) / 1e9,
+        "append_bytes": append_bytes,
+        "pool": pool,
+        "n_keys": n_keys,
+    }
+
+
+def cpu_baseline(cfg, pool_step, budget_s=12.0):
+    """The float64 oracle on a bounded sample of one steady step: whole query tiles, all heads."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    F, L, W, A = cfg.frames_per_step, cfg.tokens_per_frame, cfg.window_frames, cfg.anchor_frames
+    win = oracle.FrameListWindow(L, W, A)
+    for s in range(pool_step + 1):
+        _, kb, vb = draw_step_tensors(cfg, s)
+        win.append(bf16_bits_to_f32(kb), bf16_bits_to_f32(vb), F)
+    qb, _, _ = draw_step_tensors(cfg, pool_step)
+    q = bf16_bits_to_f32(qb)
+    kk, vv = win.keys_values()
+    n_k = kk.shape[0]
+    mask = None
+    if cfg.mask_pct is not None:
+        mask = make_block_mask(cfg.index, pool_step, cfg.n_q_heads, cfg.q_tokens, n_k, cfg.mask_pct)
+    n_qt = -(-cfg.q_tokens // TILE)
+
+    def timed(tiles):
+        rows = np.concatenate([np.arange(t * TILE, min((t + 1) * TILE, cfg.q_tokens)) for t in tiles])
+        t0 = time.perf_counter()
+        oracle.attend(q, kk, vv, mask, rows=rows)
+        dt = time.perf_counter() - t0
+        fl = sum(executed_flops(min(TILE, cfg.q_tokens - t * TILE), n_k, cfg.n_q_heads, cfg.head_dim,
+                                None if mask is None else mask[:, t:t + 1, :]) for t in tiles)
+        return dt, fl
+
+    t1, _ = timed([0])                                   # calibration: one query tile
+    n = int(max(1, min(n_qt - 1, budget_s / max(t1, 1e-3))))
+    tiles = list(range(1, 1 + n)) if n_qt > 1 else [0]
+    t_total, done_flops = timed(tiles)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    tflops = done_flops / t_total / 1e12
+    step_flops = executed_flops(cfg.q_tokens, n_k, cfg.n_q_heads, cfg.head_dim, mask)
+    return {
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{cfg.name} step {pool_step}: query tiles {tiles[0]}..{tiles[-1]} of {n_qt}, all {cfg.n_q_heads} heads "
+                  f"({done_flops / 1e9:.1f} GFLOP in {t_total:.1f} s, float64 numpy, BLAS matmul)",
+        "frames_per_s": F * (done_flops / step_flops) / t_total,
+    }
+
+
+def summary(r):
+    cfg = r["cfg"]
+    return {
+        "workload": f"{cfg.name} chunk: {cfg.n_q_heads}x{cfg.head_dim} heads (KV {cfg.n_kv_heads}), "
+                    f"{cfg.grid[0]}x{cfg.grid[1]} tokens/frame, {cfg.frames_per_step} frames/step, "
+                    f"window {cfg.window_frames} frames + anchor {cfg.anchor_frames}, "
+                    + (f"{cfg.mask_pct}% block mask" if cfg.mask_pct else "dense"),
+        "q_tokens": cfg.q_tokens,
+        "keys": steady_keys(cfg),
+        "ms_per_step": r["ms_per_step"],
+        "tflops": r["tflops"],
+        "pct_peak_step": 100 * r["tflops"] / PEAK_BF16_TFLOPS,
+        "attn_kernel_ms": r["attn_ms"],
+        "attn_kernel_tflops": r["attn_tflops"],
+        "pct_peak_attn_kernel": 100 * r["attn_tflops"] / PEAK_BF16_TFLOPS,
+        "frames_per_s": r["frames_per_s"],
+        "append_ms": r["append_ms"],
+        "append_gbs": r["append_gbs"],
+        "gflop_per_step": r["flops_per_step"] / 1e9,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="2k", choices=[c.name for c in CONFIGS])
+    ap.add_argument("--also", default="1k", help="comma-separated extra workloads reported under 'also' ('' = none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work in the CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.init()
+    cfg = {c.name: c for c in CONFIGS}[args.workload]
+    main_r = run_workload(cfg, args.warmup, args.steps)
+    also = {}
+    for name in [n for n in args.also.split(",") if n and n != cfg.name]:
+        r = run_workload({c.name: c for c in CONFIGS}[name], args.warmup, args.steps)
+        also[name] = summary(r)
+        del r
+    cpu = None
+    if not args.no_cpu_baseline:
+        fill = -(-(cfg.anchor_frames + cfg.window_frames) // cfg.frames_per_step)
+        cpu = cpu_baseline(cfg, fill, args.cpu_budget)
+
+    s = summary(main_r)
+    line = {
+        "metric": METRIC,
+        "value": round(main_r["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v rounded to bf16, seeded block masks)",
+        "config": {"workload": s["workload"], "q_tokens": s["q_tokens"], "keys": s["keys"],
+                   "gflop_per_step": round(s["gflop_per_step"], 2)},
+        "pct_peak": round(100 * main_r["tflops"] / PEAK_BF16_TFLOPS, 2),
+        "frames_per_s": round(main_r["frames_per_s"], 2),
+        "append_gbs": round(main_r["append_gbs"], 1),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_kernel<128>",
+            "achieved": round(main_r["attn_tflops"], 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(main_r["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "launch_ms": round(main_r["attn_ms"], 4),
+        },
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

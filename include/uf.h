@@ -1,0 +1,226 @@
+/*
+ * uf.h -- C ABI of libuf: chunk-causal attention over a bounded rolling KV
+ * cache on one AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  A stream is processed in steps.  Each step appends the
+ * keys and values of some whole latent frames to a cache, then lets queries
+ * attend to the keys the cache currently exposes:
+ *
+ *   out[i, h, :] = sum_j softmax_j( q[i,h,:] . k[j,g,:] / sqrt(d) ) v[j,g,:]
+ *
+ * over the visible keys j, with g = floor(h * Hkv / Hq) (grouped-query
+ * attention, consecutive query heads sharing a KV head).
+ *   - FlashDecoder review, "Rolling KV cache" and Eq. 4: the cache keeps a
+ *     fixed window of W frames (the current frames included) per KV group,
+ *     so memory and latency do not grow with the video length.
+ *   - FlashDecoder review, Algorithm 1: the update keeps the newest frames
+ *     and appends the new frame's K/V after them; keys are ordered oldest
+ *     to newest.
+ *   - FlashDecoder review, "causality by processing order": no mask inside
+ *     the window; queries see every visible key, their own frames included.
+ *   - HiStream summary, innovation 2 (anchor-guided sliding window): the
+ *     first A frames appended stay pinned as an anchor ahead of the window.
+ *   - Ultra Flash notes, key design 3 (dynamic block-sparse causal
+ *     attention): an optional mask over 128-token blocks says which
+ *     (query tile, key tile) pairs are computed at all.
+ *   - Ultra Flash notes, key design 4 (dynamic cache management, item iii):
+ *     the recent window can be cropped at run time.
+ *
+ * Conventions for every call.
+ *   - Device memory is owned by the caller: cache storage, workspace, q,
+ *     k/v inputs, outputs and masks.  The library owns only the host-side
+ *     handle.  It never allocates or frees device memory, never
+ *     synchronises, never reads device memory on the host, and launches
+ *     only on the stream it is given (NULL = the null stream).
+ *   - Calls that take a stream return once their kernels are queued.  The
+ *     caller orders appends and steps on one stream (or with events).
+ *   - Arguments are validated on the host before anything is launched.  On
+ *     any error nothing is launched, the cache state is unchanged, a
+ *     negative uf_status is returned and uf_last_error() describes it.
+ *   - Handles are not thread-safe; distinct handles may be used from
+ *     distinct threads.  No C++ exception crosses this interface.
+ *   - bf16 means IEEE-754 binary32 truncated to its upper 16 bits (bfloat16).
+ */
+#ifndef UF_H
+#define UF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum uf_status {
+  UF_OK = 0,
+  UF_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad flag, misaligned pointer */
+  UF_ERR_SHAPE = -2,        /* sizes disagree with each other or with the cache */
+  UF_ERR_DTYPE = -3,        /* element type other than UF_BF16 */
+  UF_ERR_CAPACITY = -4,     /* more frames than the ring holds, or index ranges beyond 2^31 */
+  UF_ERR_STATE = -5,        /* call not valid in the cache's current state */
+  UF_ERR_HIP = -6,          /* the HIP runtime reported an error (message in uf_last_error) */
+  UF_ERR_UNSUPPORTED = -7   /* valid request this build does not implement (e.g. head_dim) */
+} uf_status;
+
+typedef enum uf_dtype { UF_BF16 = 0 } uf_dtype;
+
+/* Flags of uf_kvcache_append. */
+#define UF_APPEND_OVERWRITE_NEWEST 1u /* rewrite the newest append's frames in place; counter unchanged */
+#define UF_APPEND_COMMIT_ONLY 2u      /* the caller already wrote the frames at the rows that
+                                         uf_kvcache_plan_append reports: advance the counter, copy nothing */
+
+#define UF_TILE 128            /* block-mask tile, in tokens */
+#define UF_MAX_APPEND_FRAMES 64 /* frames per uf_kvcache_append call */
+
+typedef struct uf_kvcache uf_kvcache; /* opaque host handle */
+
+/*
+ * A device tensor of bf16 in token-major layout [n_tokens, n_heads, head_dim]
+ * (the layout a token-wise projection produces, FlashDecoder review, Eq. 3).
+ * Element (t, h, c) is at data + t*stride_token + h*stride_head + c; strides
+ * are in elements.  The head_dim axis is contiguous.  data must be 16-byte
+ * aligned and both strides multiples of 8 elements.
+ */
+typedef struct uf_tensor {
+  void* data;
+  int32_t dtype;     /* uf_dtype */
+  int32_t n_tokens;
+  int32_t n_heads;
+  int32_t head_dim;
+  int64_t stride_token;
+  int64_t stride_head;
+} uf_tensor;
+
+/*
+ * Cache description.  Storage for K and for V is caller-allocated device
+ * memory of uf_kvcache_storage_bytes(desc) bytes each, laid out head-major
+ * [n_kv_heads][(anchor_frames + window_frames) * tokens_per_frame][head_dim]
+ * bf16 (FlashDecoder review, Eq. 4: K_t, V_t in R^{G x (W L) x D_h}).  Rows
+ * [0, A*L) hold the anchor frames in append order; rows [A*L, (A+W)*L) are
+ * the ring, frame r (counting non-anchor frames from 0) in slot r mod W.
+ * The workspace (optional, may be NULL with workspace_bytes 0) holds
+ * split-KV partial results; uf_attn_workspace_bytes gives the size that
+ * lets the library split whenever it wants to.  Must be 256-byte aligned.
+ */
+typedef struct uf_kvcache_desc {
+  int32_t n_kv_heads;       /* G >= 1 */
+  int32_t head_dim;         /* 64 or 128 */
+  int32_t tokens_per_frame; /* L = H' * W' >= 1 */
+  int32_t window_frames;    /* W >= 1: recent frames visible, the newest append included */
+  int32_t anchor_frames;    /* A >= 0: first frames appended, pinned for the whole stream */
+  void* k_storage;
+  void* v_storage;
+  void* workspace;
+  size_t workspace_bytes;
+} uf_kvcache_desc;
+
+/*
+ * Block mask over 128x128-token tiles, uint8 in device memory, 0 = skip,
+ * nonzero = keep (Ultra Flash notes, key design 3: per-head kept blocks).
+ * Element (h, qb, kb) is at data + h*stride_head + qb*stride_qblock + kb.
+ * n_heads is 1 (one mask shared by all query heads) or the query head
+ * count.  n_q_blocks must equal ceil(Nq / 128) and n_k_blocks
+ * ceil(n_keys / 128) for the step, tiles taken in query order and in key
+ * order (anchor keys, then the recent frames oldest to newest).  A query
+ * whose row keeps no tile outputs zeros.
+ */
+typedef struct uf_block_mask {
+  const uint8_t* data;
+  int32_t n_heads;
+  int32_t n_q_blocks;
+  int32_t n_k_blocks;
+  int64_t stride_head;
+  int64_t stride_qblock;
+} uf_block_mask;
+
+/*
+ * The keys a step would see now, in key order: anchor_keys anchor rows,
+ * then ring_keys recent rows.  Recent key i (0-based) lives in storage row
+ * anchor_frames*L + ((i + ring_rotation_keys) mod ring_capacity_keys).
+ */
+typedef struct uf_window_info {
+  int64_t frames_appended;
+  int32_t n_keys;
+  int32_t anchor_keys;
+  int32_t ring_keys;
+  int32_t ring_capacity_keys;   /* window_frames * tokens_per_frame */
+  int32_t ring_rotation_keys;
+  int32_t last_append_frames;
+  int32_t active_frames;        /* the crop set by uf_kvcache_set_window (default window_frames) */
+} uf_window_info;
+
+/* Where the frames of the next append would go (uf_kvcache_plan_append). */
+typedef struct uf_append_plan {
+  int32_t n_frames;
+  int32_t first_row[UF_MAX_APPEND_FRAMES]; /* storage row of each frame's first token */
+  uf_window_info window_after;
+} uf_append_plan;
+
+/* Bytes of K storage (same for V) for this description; 0 if it is invalid. */
+size_t uf_kvcache_storage_bytes(const uf_kvcache_desc* desc);
+
+/* Workspace bytes that let every step split its key range as it sees fit
+ * (proportional to head_dim, independent of sequence sizes); 0 if invalid. */
+size_t uf_attn_workspace_bytes(const uf_kvcache_desc* desc);
+
+/* Validate desc and create a handle with no frames appended.  The storage
+ * contents are not touched.  *out is set only on UF_OK. */
+uf_status uf_kvcache_create(const uf_kvcache_desc* desc, uf_kvcache** out);
+
+/* Free the handle (NULL is accepted).  The caller frees the device memory. */
+uf_status uf_kvcache_destroy(uf_kvcache* cache);
+
+/* Start a new stream: frame counter and crop back to their initial values.
+ * Storage is left as it is; a later step only reads rows appended since. */
+uf_status uf_kvcache_reset(uf_kvcache* cache);
+
+/* Crop the recent window to its newest active_frames frames, 1..window_frames
+ * (Ultra Flash notes, key design 4, item iii).  Takes effect at the next step. */
+uf_status uf_kvcache_set_window(uf_kvcache* cache, int32_t active_frames);
+
+/*
+ * Append n_frames whole frames of keys and values (FlashDecoder review,
+ * Algorithm 1, cache update).  k_new and v_new are [n_frames*L, n_kv_heads,
+ * head_dim] bf16.  The first anchor_frames frames ever appended go to the
+ * anchor rows; later frames go to ring slot (r mod W).  At most W ring frames
+ * per call and UF_MAX_APPEND_FRAMES in all.  n_frames == 0 is a no-op.
+ * flags: 0, UF_APPEND_OVERWRITE_NEWEST (n_frames must equal the last
+ * append's count; the same rows are rewritten, the counter does not move),
+ * or UF_APPEND_COMMIT_ONLY (k_new and v_new must be NULL; nothing is copied).
+ * One kernel launch on `stream` (none for COMMIT_ONLY); the host frame
+ * counter advances when the call returns UF_OK.
+ */
+uf_status uf_kvcache_append(uf_kvcache* cache, const uf_tensor* k_new, const uf_tensor* v_new,
+                            int32_t n_frames, uint32_t flags, void* stream);
+
+/* Host-only: the storage rows the next append of n_frames frames with these
+ * flags would write, and the window it would leave.  Changes nothing. */
+uf_status uf_kvcache_plan_append(const uf_kvcache* cache, int32_t n_frames, uint32_t flags,
+                                 uf_append_plan* out);
+
+/* Host-only: the window a step would see now. */
+uf_status uf_kvcache_window(const uf_kvcache* cache, uf_window_info* out);
+
+/*
+ * One attention step: every query row of q attends to the cache's visible
+ * keys (optionally restricted by block_mask, NULL = all keys).  q and out
+ * are [Nq, Hq, head_dim] bf16 with Hq a multiple of n_kv_heads; out must not
+ * overlap q or the cache.  Nq == 0 is a no-op.  Accumulation is fp32: scores
+ * and the online softmax in fp32, probabilities rounded to bf16 for the
+ * P.V product, output rounded to bf16 (nearest even).  UF_ERR_STATE if no
+ * frame has been appended.  One or two kernel launches on `stream`.
+ */
+uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mask* block_mask,
+                       uf_tensor* out, void* stream);
+
+/* Static string naming a status code. */
+const char* uf_status_string(uf_status status);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* uf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UF_H */

@@ -1,0 +1,211 @@
+"""CPU tests of libuf's host side: exports, validation and window bookkeeping.
+
+No kernel runs here.  Calls that would launch are only made with arguments
+that fail validation (which happens before any launch), or with
+UF_APPEND_COMMIT_ONLY, which launches nothing.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import visible_frames_after
+from tests.ring_model import RingModel
+from windowed_attention_amd import uf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = uf.raw_lib()
+FAKE = 1 << 20  # an aligned address that is never dereferenced: every call using it fails validation first
+KS, VS = 1 << 40, 2 << 40  # fake cache storage, far from every other fake address
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "uf.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(uf_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 12, names
+    assert sorted(uf.EXPORTED) == names
+    out = subprocess.run(["nm", "-D", "--defined-only", uf._LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (uf_\w+)$", out, flags=re.M))
+    for n in names:
+        assert n in exported, n
+        assert getattr(LIB, n) is not None
+
+
+def test_status_strings():
+    for code in range(0, -8, -1):
+        assert uf.uf_status_string(code).startswith("UF_")
+    assert uf.uf_status_string(-5) == "UF_ERR_STATE"
+
+
+def desc(H=2, d=128, L=64, W=3, A=0, k=KS, v=VS, ws=None, ws_bytes=0):
+    return uf.uf_kvcache_desc(H, d, L, W, A, k, v, ws, ws_bytes)
+
+
+def create(**kw):
+    h = ctypes.c_void_p()
+    st = LIB.uf_kvcache_create(ctypes.byref(desc(**kw)), ctypes.byref(h))
+    return st, h.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), uf.UF_ERR_UNSUPPORTED),
+    (dict(H=0), uf.UF_ERR_SHAPE),
+    (dict(L=0), uf.UF_ERR_SHAPE),
+    (dict(W=0), uf.UF_ERR_SHAPE),
+    (dict(A=-1), uf.UF_ERR_SHAPE),
+    (dict(k=None), uf.UF_ERR_INVALID_ARG),
+    (dict(k=KS + 8), uf.UF_ERR_INVALID_ARG),
+    (dict(v=KS + 64), uf.UF_ERR_INVALID_ARG),           # overlaps k storage
+    (dict(ws_bytes=1024), uf.UF_ERR_INVALID_ARG),          # size without a pointer
+    (dict(ws=FAKE * 8 + 16, ws_bytes=1024), uf.UF_ERR_INVALID_ARG),  # misaligned workspace
+    (dict(L=1 << 20, W=4096), uf.UF_ERR_CAPACITY),
+])
+def test_create_rejects(kw, status):
+    st, h = create(**kw)
+    assert st == status, uf.uf_last_error()
+    assert h is None
+    assert uf.uf_last_error() != ""
+
+
+def test_sizes():
+    d = desc(H=3, d=128, L=1560, W=2, A=0)
+    assert uf.uf_kvcache_storage_bytes(d) == 3 * 2 * 1560 * 128 * 2
+    d = desc(H=12, d=128, L=1560, W=9, A=3)
+    assert uf.uf_kvcache_storage_bytes(d) == 12 * 12 * 1560 * 128 * 2
+    assert uf.uf_attn_workspace_bytes(d) > 0
+    assert uf.uf_kvcache_storage_bytes(desc(d=80)) == 0
+
+
+def _window(h):
+    return uf.uf_kvcache_window(h).as_dict()
+
+
+def _check_window(h, model, W, A, L, active):
+    w = uf.uf_kvcache_window(h)
+    vis = visible_frames_after(model.count, W, A, active)
+    assert w.frames_appended == model.count
+    assert w.n_keys == len(vis) * L
+    assert w.anchor_keys == min(A, model.count) * L
+    assert w.ring_keys == w.n_keys - w.anchor_keys
+    assert w.ring_capacity_keys == W * L
+    # physical row of every visible key, from the header's formula vs the frame-by-frame model
+    i = np.arange(w.n_keys)
+    rows = np.where(i < w.anchor_keys, i,
+                    A * L + (i - w.anchor_keys + w.ring_rotation_keys) % max(1, w.ring_capacity_keys))
+    assert np.array_equal(rows, model.visible_rows(vis))
+
+
+@pytest.mark.parametrize("L,W,A,F", [(64, 3, 0, 1), (1560, 9, 3, 3), (1560, 2, 0, 1), (6240, 6, 0, 3),
+                                     (7, 5, 2, 3), (5, 4, 1, 2), (3, 1, 0, 1)])
+def test_window_bookkeeping(L, W, A, F):
+    st, h = create(H=1, d=64, L=L, W=W, A=A)
+    assert st == uf.UF_OK
+    model = RingModel(1, 64, L, W, A)
+    try:
+        for step in range(3 * (W + A) + 2):
+            plan = uf.uf_kvcache_plan_append(h, F)
+            frames = model.append(F)
+            assert [plan.first_row[i] for i in range(F)] == [model.first_row(f) for f in frames]
+            uf.uf_kvcache_append(h, None, None, F, uf.UF_APPEND_COMMIT_ONLY, 0)
+            assert plan.window_after.as_dict() == _window(h)
+            _check_window(h, model, W, A, L, W)
+            if W > 1 and step % 3 == 2:           # crop the recent window, then restore it
+                uf.uf_kvcache_set_window(h, W - 1)
+                _check_window(h, model, W, A, L, W - 1)
+                uf.uf_kvcache_set_window(h, W)
+        # overwrite of the newest append: same rows, counter unchanged
+        before = _window(h)
+        plan = uf.uf_kvcache_plan_append(h, F, uf.UF_APPEND_OVERWRITE_NEWEST)
+        assert [plan.first_row[i] for i in range(F)] == [model.first_row(f) for f in range(model.count - F, model.count)]
+        uf.uf_kvcache_append(h, None, None, F, uf.UF_APPEND_OVERWRITE_NEWEST | uf.UF_APPEND_COMMIT_ONLY, 0)
+        assert _window(h) == before
+        uf.uf_kvcache_reset(h)
+        w = _window(h)
+        assert w["frames_appended"] == 0 and w["n_keys"] == 0 and w["active_frames"] == W
+    finally:
+        uf.uf_kvcache_destroy(h)
+
+
+def _tensor(n_tok, heads, d=128, data=FAKE, dtype=uf.UF_BF16, st=None, sh=None):
+    return uf.uf_tensor(data, dtype, n_tok, heads, d, heads * d if st is None else st, d if sh is None else sh)
+
+
+def test_append_validation_leaves_state_unchanged():
+    st, h = create(H=2, d=128, L=16, W=3, A=1)
+    assert st == uf.UF_OK
+    try:
+        uf.uf_kvcache_append(h, None, None, 2, uf.UF_APPEND_COMMIT_ONLY, 0)
+        before = _window(h)
+        ok_k, ok_v = _tensor(32, 2), _tensor(32, 2, data=FAKE * 4)
+        bad = [
+            (ok_k, ok_v, 2, 0x8, uf.UF_ERR_INVALID_ARG),                       # unknown flag
+            (ok_k, ok_v, -1, 0, uf.UF_ERR_INVALID_ARG),
+            (_tensor(80, 2), _tensor(80, 2), 5, 0, uf.UF_ERR_CAPACITY),       # 4 ring frames > W = 3
+            (ok_k, ok_v, 65, 0, uf.UF_ERR_CAPACITY),
+            (_tensor(16, 2), _tensor(16, 2), 1, uf.UF_APPEND_OVERWRITE_NEWEST, uf.UF_ERR_STATE),  # newest had 2
+            (_tensor(31, 2), ok_v, 2, 0, uf.UF_ERR_SHAPE),                     # token count
+            (_tensor(32, 3), ok_v, 2, 0, uf.UF_ERR_SHAPE),                     # head count
+            (_tensor(32, 2, d=64), ok_v, 2, 0, uf.UF_ERR_SHAPE),               # head_dim
+            (_tensor(32, 2, dtype=7), ok_v, 2, 0, uf.UF_ERR_DTYPE),
+            (_tensor(32, 2, data=FAKE + 2), ok_v, 2, 0, uf.UF_ERR_INVALID_ARG),  # misaligned
+            (_tensor(32, 2, st=260), ok_v, 2, 0, uf.UF_ERR_INVALID_ARG),        # stride not a multiple of 8
+            (_tensor(32, 2, data=None), ok_v, 2, 0, uf.UF_ERR_INVALID_ARG),
+            (ok_k, ok_v, 2, uf.UF_APPEND_COMMIT_ONLY, uf.UF_ERR_INVALID_ARG),   # commit-only with tensors
+        ]
+        for k, v, n, flags, want in bad:
+            got = LIB.uf_kvcache_append(h, ctypes.byref(k), ctypes.byref(v), n, flags, None)
+            assert got == want, (n, flags, uf.uf_status_string(got), uf.uf_last_error())
+            assert _window(h) == before
+        assert LIB.uf_kvcache_append(None, None, None, 1, 0, None) == uf.UF_ERR_INVALID_ARG
+        assert LIB.uf_kvcache_append(h, None, None, 0, 0, None) == uf.UF_OK   # empty append is a no-op
+        assert _window(h) == before
+        assert LIB.uf_kvcache_set_window(h, 0) == uf.UF_ERR_SHAPE
+        assert LIB.uf_kvcache_set_window(h, 4) == uf.UF_ERR_SHAPE
+        assert _window(h) == before
+    finally:
+        uf.uf_kvcache_destroy(h)
+
+
+def _mask(n_heads, nqb, nkb, data=FAKE * 16):
+    return uf.uf_block_mask(data, n_heads, nqb, nkb, nqb * nkb, nkb)
+
+
+def test_step_validation():
+    st, h = create(H=2, d=128, L=100, W=3, A=0)
+    assert st == uf.UF_OK
+    q, out = _tensor(200, 4, data=FAKE * 32), _tensor(200, 4, data=FAKE * 64)
+    try:
+        # no frame appended yet
+        assert LIB.uf_attn_step(ctypes.byref(q), h, None, ctypes.byref(out), None) == uf.UF_ERR_STATE
+        uf.uf_kvcache_append(h, None, None, 2, uf.UF_APPEND_COMMIT_ONLY, 0)  # 200 keys: 2 tiles
+        cases = [
+            (_tensor(200, 3, data=FAKE * 32), _tensor(200, 3, data=FAKE * 64), None, uf.UF_ERR_SHAPE),  # 3 % 2
+            (q, _tensor(199, 4, data=FAKE * 64), None, uf.UF_ERR_SHAPE),
+            (q, _tensor(200, 4, d=64, data=FAKE * 64), None, uf.UF_ERR_SHAPE),
+            (q, q, None, uf.UF_ERR_INVALID_ARG),                                         # out aliases q
+            (q, _tensor(200, 4, data=KS + 256), None, uf.UF_ERR_INVALID_ARG),           # out overlaps K storage
+            (q, out, _mask(4, 2, 3), uf.UF_ERR_SHAPE),                                    # 3 key tiles, want 2
+            (q, out, _mask(4, 1, 2), uf.UF_ERR_SHAPE),                                    # 1 query tile, want 2
+            (q, out, _mask(2, 2, 2), uf.UF_ERR_SHAPE),                                    # heads neither 1 nor 4
+            (q, out, _mask(4, 2, 2, data=None), uf.UF_ERR_INVALID_ARG),
+            (_tensor(200, 4, data=FAKE * 32, dtype=3), out, None, uf.UF_ERR_DTYPE),
+        ]
+        for qq, oo, m, want in cases:
+            mp = None if m is None else ctypes.byref(m)
+            got = LIB.uf_attn_step(ctypes.byref(qq), h, mp, ctypes.byref(oo), None)
+            assert got == want, (uf.uf_status_string(got), uf.uf_last_error())
+        assert LIB.uf_attn_step(None, h, None, ctypes.byref(out), None) == uf.UF_ERR_INVALID_ARG
+        assert LIB.uf_attn_step(ctypes.byref(q), None, None, ctypes.byref(out), None) == uf.UF_ERR_INVALID_ARG
+        # an empty query set is valid and launches nothing
+        e = _tensor(0, 4, data=FAKE * 32)
+        assert LIB.uf_attn_step(ctypes.byref(e), h, None, ctypes.byref(_tensor(0, 4, data=FAKE * 64)), None) == uf.UF_OK
+    finally:
+        uf.uf_kvcache_destroy(h)

@@ -1,0 +1,408 @@
+// Host side of libuf: argument validation, the rolling-window bookkeeping
+// and launch configuration.  See include/uf.h for the contract of each call.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+
+#include "uf.h"
+#include "uf_internal.h"
+
+struct uf_kvcache {
+  uf_kvcache_desc d;
+  int64_t frames;       // frames appended since create / reset
+  int32_t last_append;  // frames in the newest append
+  int32_t active;       // recent frames visible (crop), 1..W
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+uf_status fail(uf_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+uf_status hip_fail(hipError_t e, const char* what) {
+  return fail(UF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxIndex = (int64_t)1 << 31;
+// Split partials are budgeted in (query, head) rows: at most this many rows
+// times splits, which bounds the workspace independently of the step size.
+constexpr int64_t kSplitRowBudget = 1024 * 128;
+constexpr int kMaxSplits = 16;
+
+uf_status check_desc(const uf_kvcache_desc* d) {
+  if (!d) return fail(UF_ERR_INVALID_ARG, "desc is NULL");
+  if (d->n_kv_heads < 1) return fail(UF_ERR_SHAPE, "n_kv_heads must be >= 1 (got %d)", d->n_kv_heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(UF_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
+  if (d->tokens_per_frame < 1) return fail(UF_ERR_SHAPE, "tokens_per_frame must be >= 1");
+  if (d->window_frames < 1) return fail(UF_ERR_SHAPE, "window_frames must be >= 1");
+  if (d->anchor_frames < 0) return fail(UF_ERR_SHAPE, "anchor_frames must be >= 0");
+  const int64_t rows = (int64_t)(d->anchor_frames + (int64_t)d->window_frames) * d->tokens_per_frame;
+  if (rows >= kMaxIndex || rows * d->head_dim >= kMaxIndex * 64)
+    return fail(UF_ERR_CAPACITY, "cache of %lld rows per head is too large", (long long)rows);
+  return UF_OK;
+}
+
+int64_t rows_per_head(const uf_kvcache_desc& d) {
+  return ((int64_t)d.anchor_frames + d.window_frames) * d.tokens_per_frame;
+}
+
+// Window after `frames` frames appended with a crop of `active` recent frames.
+uf_window_info window_of(const uf_kvcache_desc& d, int64_t frames, int32_t last_append, int32_t active) {
+  uf_window_info w;
+  memset(&w, 0, sizeof w);
+  const int64_t L = d.tokens_per_frame;
+  const int64_t anchors = std::min<int64_t>(frames, d.anchor_frames);
+  const int64_t recent_total = frames - anchors;
+  const int64_t recent = std::min<int64_t>(recent_total, active);
+  const int64_t oldest = recent_total - recent;  // recent-frame index of the oldest visible one
+  w.frames_appended = frames;
+  w.anchor_keys = (int32_t)(anchors * L);
+  w.ring_keys = (int32_t)(recent * L);
+  w.n_keys = w.anchor_keys + w.ring_keys;
+  w.ring_capacity_keys = (int32_t)((int64_t)d.window_frames * L);
+  w.ring_rotation_keys = (int32_t)((oldest % d.window_frames) * L);
+  w.last_append_frames = last_append;
+  w.active_frames = active;
+  return w;
+}
+
+int64_t first_row_of_frame(const uf_kvcache_desc& d, int64_t frame) {
+  const int64_t slot = frame < d.anchor_frames ? frame
+                                               : d.anchor_frames + (frame - d.anchor_frames) % d.window_frames;
+  return slot * d.tokens_per_frame;
+}
+
+uf_status check_append_request(const uf_kvcache* c, int32_t n_frames, uint32_t flags) {
+  if (flags & ~(UF_APPEND_OVERWRITE_NEWEST | UF_APPEND_COMMIT_ONLY))
+    return fail(UF_ERR_INVALID_ARG, "unknown append flags 0x%x", flags);
+  if (n_frames < 0) return fail(UF_ERR_INVALID_ARG, "n_frames must be >= 0");
+  if (n_frames > UF_MAX_APPEND_FRAMES)
+    return fail(UF_ERR_CAPACITY, "at most %d frames per append (got %d)", UF_MAX_APPEND_FRAMES, n_frames);
+  const auto& d = c->d;
+  if (flags & UF_APPEND_OVERWRITE_NEWEST) {
+    if (n_frames != c->last_append || c->last_append == 0)
+      return fail(UF_ERR_STATE, "overwrite must cover the newest append exactly (%d frames, got %d)",
+                  c->last_append, n_frames);
+    return UF_OK;
+  }
+  const int64_t first = c->frames;
+  const int64_t anchor_left = std::max<int64_t>(0, d.anchor_frames - first);
+  const int64_t ring_frames = std::max<int64_t>(0, n_frames - anchor_left);
+  if (ring_frames > d.window_frames)
+    return fail(UF_ERR_CAPACITY, "append of %d frames puts %lld frames in a ring of %d", n_frames,
+                (long long)ring_frames, d.window_frames);
+  return UF_OK;
+}
+
+uf_status check_tensor(const uf_tensor* t, const char* name, int head_dim) {
+  if (!t) return fail(UF_ERR_INVALID_ARG, "%s is NULL", name);
+  if (t->dtype != UF_BF16) return fail(UF_ERR_DTYPE, "%s: dtype must be UF_BF16", name);
+  if (t->n_tokens < 0 || t->n_heads < 1) return fail(UF_ERR_SHAPE, "%s: bad sizes", name);
+  if (t->head_dim != head_dim)
+    return fail(UF_ERR_SHAPE, "%s: head_dim %d, cache has %d", name, t->head_dim, head_dim);
+  if (t->n_tokens > 0 && !t->data) return fail(UF_ERR_INVALID_ARG, "%s: data is NULL", name);
+  if (((uintptr_t)t->data & 15) != 0) return fail(UF_ERR_INVALID_ARG, "%s: data not 16-byte aligned", name);
+  if (t->stride_token < 0 || t->stride_head < 0 || t->stride_token % 8 || t->stride_head % 8)
+    return fail(UF_ERR_INVALID_ARG, "%s: strides must be non-negative multiples of 8 elements", name);
+  if (t->n_heads > 1 && t->stride_head < head_dim)
+    return fail(UF_ERR_SHAPE, "%s: head stride smaller than head_dim", name);
+  return UF_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const char* pa = (const char*)a;
+  const char* pb = (const char*)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+size_t tensor_extent_bytes(const uf_tensor& t) {
+  if (t.n_tokens == 0) return 0;
+  return ((size_t)(t.n_tokens - 1) * t.stride_token + (size_t)(t.n_heads - 1) * t.stride_head + t.head_dim) * 2;
+}
+
+int device_cu_count() {
+  static thread_local int cached_dev = -1, cached_cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != cached_dev) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached_dev = dev;
+    cached_cus = cus;
+  }
+  return cached_cus;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t uf_kvcache_storage_bytes(const uf_kvcache_desc* desc) {
+  if (!desc || check_desc(desc) != UF_OK) return 0;
+  return (size_t)desc->n_kv_heads * rows_per_head(*desc) * desc->head_dim * 2;
+}
+
+size_t uf_attn_workspace_bytes(const uf_kvcache_desc* desc) {
+  if (!desc || check_desc(desc) != UF_OK) return 0;
+  return (size_t)kSplitRowBudget * (desc->head_dim + 2) * sizeof(float);
+}
+
+uf_status uf_kvcache_create(const uf_kvcache_desc* desc, uf_kvcache** out) {
+  if (!out) return fail(UF_ERR_INVALID_ARG, "out is NULL");
+  uf_status s = check_desc(desc);
+  if (s != UF_OK) return s;
+  if (!desc->k_storage || !desc->v_storage) return fail(UF_ERR_INVALID_ARG, "k_storage / v_storage is NULL");
+  if (((uintptr_t)desc->k_storage & 15) || ((uintptr_t)desc->v_storage & 15))
+    return fail(UF_ERR_INVALID_ARG, "cache storage must be 16-byte aligned");
+  const size_t bytes = uf_kvcache_storage_bytes(desc);
+  if (overlaps(desc->k_storage, bytes, desc->v_storage, bytes))
+    return fail(UF_ERR_INVALID_ARG, "k_storage and v_storage overlap");
+  if (desc->workspace_bytes && !desc->workspace)
+    return fail(UF_ERR_INVALID_ARG, "workspace_bytes > 0 with a NULL workspace");
+  if ((uintptr_t)desc->workspace & 255) return fail(UF_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  uf_kvcache* c = new (std::nothrow) uf_kvcache;
+  if (!c) return fail(UF_ERR_INVALID_ARG, "out of host memory");
+  c->d = *desc;
+  c->frames = 0;
+  c->last_append = 0;
+  c->active = desc->window_frames;
+  *out = c;
+  return UF_OK;
+}
+
+uf_status uf_kvcache_destroy(uf_kvcache* cache) {
+  delete cache;
+  return UF_OK;
+}
+
+uf_status uf_kvcache_reset(uf_kvcache* cache) {
+  if (!cache) return fail(UF_ERR_INVALID_ARG, "cache is NULL");
+  cache->frames = 0;
+  cache->last_append = 0;
+  cache->active = cache->d.window_frames;
+  return UF_OK;
+}
+
+uf_status uf_kvcache_set_window(uf_kvcache* cache, int32_t active_frames) {
+  if (!cache) return fail(UF_ERR_INVALID_ARG, "cache is NULL");
+  if (active_frames < 1 || active_frames > cache->d.window_frames)
+    return fail(UF_ERR_SHAPE, "active_frames must lie in 1..%d (got %d)", cache->d.window_frames, active_frames);
+  cache->active = active_frames;
+  return UF_OK;
+}
+
+uf_status uf_kvcache_window(const uf_kvcache* cache, uf_window_info* out) {
+  if (!cache || !out) return fail(UF_ERR_INVALID_ARG, "cache or out is NULL");
+  *out = window_of(cache->d, cache->frames, cache->last_append, cache->active);
+  return UF_OK;
+}
+
+uf_status uf_kvcache_plan_append(const uf_kvcache* cache, int32_t n_frames, uint32_t flags, uf_append_plan* out) {
+  if (!cache || !out) return fail(UF_ERR_INVALID_ARG, "cache or out is NULL");
+  uf_status s = check_append_request(cache, n_frames, flags);
+  if (s != UF_OK) return s;
+  memset(out, 0, sizeof *out);
+  out->n_frames = n_frames;
+  const bool overwrite = flags & UF_APPEND_OVERWRITE_NEWEST;
+  const int64_t first = overwrite ? cache->frames - n_frames : cache->frames;
+  for (int f = 0; f < n_frames; ++f) out->first_row[f] = (int32_t)first_row_of_frame(cache->d, first + f);
+  if (overwrite || n_frames == 0)
+    out->window_after = window_of(cache->d, cache->frames, cache->last_append, cache->active);
+  else
+    out->window_after = window_of(cache->d, cache->frames + n_frames, n_frames, cache->active);
+  return UF_OK;
+}
+
+uf_status uf_kvcache_append(uf_kvcache* cache, const uf_tensor* k_new, const uf_tensor* v_new, int32_t n_frames,
+                            uint32_t flags, void* stream) {
+  if (!cache) return fail(UF_ERR_INVALID_ARG, "cache is NULL");
+  uf_status s = check_append_request(cache, n_frames, flags);
+  if (s != UF_OK) return s;
+  if (n_frames == 0) return UF_OK;
+  const auto& d = cache->d;
+  const bool overwrite = flags & UF_APPEND_OVERWRITE_NEWEST;
+  if (flags & UF_APPEND_COMMIT_ONLY) {
+    if (k_new || v_new) return fail(UF_ERR_INVALID_ARG, "UF_APPEND_COMMIT_ONLY takes NULL k_new and v_new");
+  } else {
+    if ((s = check_tensor(k_new, "k_new", d.head_dim)) != UF_OK) return s;
+    if ((s = check_tensor(v_new, "v_new", d.head_dim)) != UF_OK) return s;
+    const int64_t n_tok = (int64_t)n_frames * d.tokens_per_frame;
+    if (k_new->n_tokens != n_tok || v_new->n_tokens != n_tok)
+      return fail(UF_ERR_SHAPE, "k_new / v_new must hold n_frames * tokens_per_frame = %lld tokens",
+                  (long long)n_tok);
+    if (k_new->n_heads != d.n_kv_heads || v_new->n_heads != d.n_kv_heads)
+      return fail(UF_ERR_SHAPE, "k_new / v_new must have %d heads", d.n_kv_heads);
+    if (n_tok * (d.head_dim / 8) * d.n_kv_heads >= kMaxIndex)
+      return fail(UF_ERR_CAPACITY, "append too large for one launch");
+    uf::AppendParams p;
+    p.src[0] = (const uint16_t*)k_new->data;
+    p.src[1] = (const uint16_t*)v_new->data;
+    p.src_stride_tok[0] = k_new->stride_token;
+    p.src_stride_tok[1] = v_new->stride_token;
+    p.src_stride_head[0] = k_new->stride_head;
+    p.src_stride_head[1] = v_new->stride_head;
+    p.dst[0] = (uint16_t*)d.k_storage;
+    p.dst[1] = (uint16_t*)d.v_storage;
+    p.rows_total = rows_per_head(d);
+    p.n_tok = (int32_t)n_tok;
+    p.n_heads = d.n_kv_heads;
+    p.head_dim = d.head_dim;
+    p.tokens_per_frame = d.tokens_per_frame;
+    p.anchor_frames = d.anchor_frames;
+    p.window_frames = d.window_frames;
+    p.first_frame = overwrite ? cache->frames - n_frames : cache->frames;
+    hipError_t e = uf::launch_append(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+  }
+  if (!overwrite) {
+    cache->frames += n_frames;
+    cache->last_append = n_frames;
+  }
+  return UF_OK;
+}
+
+uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mask* mask, uf_tensor* out,
+                       void* stream) {
+  if (!cache) return fail(UF_ERR_INVALID_ARG, "cache is NULL");
+  const auto& d = cache->d;
+  uf_status s;
+  if ((s = check_tensor(q, "q", d.head_dim)) != UF_OK) return s;
+  if ((s = check_tensor(out, "out", d.head_dim)) != UF_OK) return s;
+  if (out->n_tokens != q->n_tokens || out->n_heads != q->n_heads)
+    return fail(UF_ERR_SHAPE, "out must have q's shape");
+  if (q->n_heads % d.n_kv_heads != 0)
+    return fail(UF_ERR_SHAPE, "query heads (%d) must be a multiple of KV heads (%d)", q->n_heads, d.n_kv_heads);
+  const uf_window_info w = window_of(d, cache->frames, cache->last_append, cache->active);
+  if (w.n_keys == 0) return fail(UF_ERR_STATE, "no frame appended yet");
+  const int32_t n_q = q->n_tokens, hq = q->n_heads;
+  if ((int64_t)n_q * hq >= kMaxIndex) return fail(UF_ERR_CAPACITY, "too many query rows");
+  const size_t out_bytes = tensor_extent_bytes(*out);
+  const size_t kv_bytes = uf_kvcache_storage_bytes(&d);
+  if (overlaps(out->data, out_bytes, q->data, tensor_extent_bytes(*q)) ||
+      overlaps(out->data, out_bytes, d.k_storage, kv_bytes) || overlaps(out->data, out_bytes, d.v_storage, kv_bytes))
+    return fail(UF_ERR_INVALID_ARG, "out overlaps q or the cache");
+  const int n_qt = (n_q + UF_TILE - 1) / UF_TILE;
+  const int n_kt = (w.n_keys + UF_TILE - 1) / UF_TILE;
+  if (mask) {
+    if (!mask->data) return fail(UF_ERR_INVALID_ARG, "mask data is NULL");
+    if (mask->n_heads != 1 && mask->n_heads != hq)
+      return fail(UF_ERR_SHAPE, "mask n_heads must be 1 or %d (got %d)", hq, mask->n_heads);
+    if (mask->n_q_blocks != n_qt || mask->n_k_blocks != n_kt)
+      return fail(UF_ERR_SHAPE, "mask must be %d x %d tiles for this step (got %d x %d)", n_qt, n_kt,
+                  mask->n_q_blocks, mask->n_k_blocks);
+    if (mask->stride_head < 0 || mask->stride_qblock < 0)
+      return fail(UF_ERR_INVALID_ARG, "mask strides must be non-negative");
+  }
+  if (n_q == 0) return UF_OK;
+
+  const int group = hq / d.n_kv_heads;
+  const bool per_head_mask = mask && mask->n_heads > 1;
+  int hpw = 1;
+  if (!per_head_mask) hpw = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+  if (const char* e = getenv("UF_HEADS_PER_WG")) {
+    const int v = atoi(e);
+    if ((v == 1 || v == 2 || v == 4) && group % v == 0 && (v == 1 || !per_head_mask)) hpw = v;
+  }
+  const int qpw = UF_TILE / hpw;
+  const int n_qblk = (n_q + qpw - 1) / qpw;
+  const int n_hgrp = hq / hpw;
+  const int64_t items = (int64_t)n_qblk * n_hgrp;
+
+  // Split the key range when the work items alone leave CUs idle.
+  int splits = 1;
+  const int cus = device_cu_count();
+  if (items < 2 * cus) {
+    splits = (int)std::min<int64_t>((2 * cus + items - 1) / items, kMaxSplits);
+    splits = std::min(splits, std::max(1, n_kt / 4));
+  }
+  if (const char* e = getenv("UF_SPLITS")) {
+    const int v = atoi(e);
+    if (v >= 1 && v <= kMaxSplits) splits = std::min(v, n_kt);
+  }
+  const int64_t rows = (int64_t)n_q * hq;
+  while (splits > 1 && ((int64_t)splits * rows * (d.head_dim + 2) * (int64_t)sizeof(float) > (int64_t)d.workspace_bytes))
+    --splits;
+  if (items * splits >= kMaxIndex) return fail(UF_ERR_CAPACITY, "grid too large");
+
+  uf::AttnParams p;
+  p.q = (const uint16_t*)q->data;
+  p.q_stride_tok = q->stride_token;
+  p.q_stride_head = q->stride_head;
+  p.out = (uint16_t*)out->data;
+  p.o_stride_tok = out->stride_token;
+  p.o_stride_head = out->stride_head;
+  p.k = (const uint16_t*)d.k_storage;
+  p.v = (const uint16_t*)d.v_storage;
+  p.kv_head_stride = rows_per_head(d) * d.head_dim;
+  p.n_q = n_q;
+  p.n_k = w.n_keys;
+  p.n_q_heads = hq;
+  p.group = group;
+  p.heads_per_wg = hpw;
+  p.n_qblk = n_qblk;
+  p.n_hgrp = n_hgrp;
+  p.splits = splits;
+  p.anchor_keys = w.anchor_keys;
+  p.ring_base = d.anchor_frames * d.tokens_per_frame;
+  p.ring_cap = w.ring_capacity_keys;
+  p.ring_rot = w.ring_rotation_keys;
+  p.mask = mask ? mask->data : nullptr;
+  p.mask_heads = mask ? mask->n_heads : 1;
+  p.n_kb = n_kt;
+  p.mask_stride_head = mask ? mask->stride_head : 0;
+  p.mask_stride_q = mask ? mask->stride_qblock : 0;
+  p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d.head_dim));
+  p.ws_o = (float*)d.workspace;
+  p.ws_ml = splits > 1 ? (float*)d.workspace + (size_t)splits * rows * d.head_dim : nullptr;
+  hipError_t e = uf::launch_attention(p, d.head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (splits > 1) {
+    uf::CombineParams c;
+    c.ws_o = p.ws_o;
+    c.ws_ml = p.ws_ml;
+    c.out = p.out;
+    c.o_stride_tok = p.o_stride_tok;
+    c.o_stride_head = p.o_stride_head;
+    c.n_q = n_q;
+    c.n_q_heads = hq;
+    c.splits = splits;
+    e = uf::launch_combine(c, d.head_dim, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
+  return UF_OK;
+}
+
+const char* uf_status_string(uf_status status) {
+  switch (status) {
+    case UF_OK: return "UF_OK";
+    case UF_ERR_INVALID_ARG: return "UF_ERR_INVALID_ARG";
+    case UF_ERR_SHAPE: return "UF_ERR_SHAPE";
+    case UF_ERR_DTYPE: return "UF_ERR_DTYPE";
+    case UF_ERR_CAPACITY: return "UF_ERR_CAPACITY";
+    case UF_ERR_STATE: return "UF_ERR_STATE";
+    case UF_ERR_HIP: return "UF_ERR_HIP";
+    case UF_ERR_UNSUPPORTED: return "UF_ERR_UNSUPPORTED";
+  }
+  return "UF_ERR_UNKNOWN";
+}
+
+const char* uf_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal interface between the C ABI (uf_api.cpp) and the gfx950 kernels
+// (uf_kernels.hip).  Plain structs passed to kernels by value.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace uf {
+
+// Copy of n_tok tokens of K and V ([token][head][d], strided) into the
+// head-major cache rows of their frames.
+struct AppendParams {
+  const uint16_t* src[2];      // k_new, v_new
+  int64_t src_stride_tok[2];
+  int64_t src_stride_head[2];
+  uint16_t* dst[2];            // k_storage, v_storage
+  int64_t rows_total;          // (A + W) * L rows per head
+  int32_t n_tok;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t tokens_per_frame;    // L
+  int32_t anchor_frames;       // A
+  int32_t window_frames;       // W
+  int64_t first_frame;         // global index of the first appended frame
+};
+
+// One attention step.  The grid is a flat list of work items
+// (query block, head group, split) handed out XCD by XCD.
+struct AttnParams {
+  const uint16_t* q;
+  int64_t q_stride_tok, q_stride_head;
+  uint16_t* out;
+  int64_t o_stride_tok, o_stride_head;
+  const uint16_t* k;           // cache storage base
+  const uint16_t* v;
+  int64_t kv_head_stride;      // rows_total * head_dim
+  int32_t n_q;                 // query rows
+  int32_t n_k;                 // visible keys
+  int32_t n_q_heads;
+  int32_t group;               // Hq / Hkv
+  int32_t heads_per_wg;        // 1, 2 or 4 query heads of one KV group per work-group
+  int32_t n_qblk;              // query blocks of 128 / heads_per_wg rows
+  int32_t n_hgrp;              // n_q_heads / heads_per_wg
+  int32_t splits;              // key-range splits (1 = write out directly)
+  int32_t anchor_keys;         // logical keys [0, anchor_keys) are storage rows [0, anchor_keys)
+  int32_t ring_base;           // storage row of ring slot 0 (= A * L)
+  int32_t ring_cap;            // W * L
+  int32_t ring_rot;            // recent key i is at ring_base + (i + ring_rot) mod ring_cap
+  const uint8_t* mask;         // null = dense
+  int32_t mask_heads;          // 1 or n_q_heads
+  int32_t n_kb;                // key tiles of 128
+  int64_t mask_stride_head, mask_stride_q;
+  float scale_log2;            // log2(e) / sqrt(d)
+  float* ws_o;                 // [splits][n_q][n_q_heads][d] unnormalised partial outputs
+  float* ws_ml;                // [splits][n_q][n_q_heads][2]: running max (log2 units), sum
+};
+
+struct CombineParams {
+  const float* ws_o;
+  const float* ws_ml;
+  uint16_t* out;
+  int64_t o_stride_tok, o_stride_head;
+  int32_t n_q, n_q_heads, splits;
+};
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
+
+}  // namespace uf
