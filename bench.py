@@ -33,6 +33,10 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 F
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def executed_flops(n_q, n_k, n_q_heads, d, mask):
     """4*d per (query, key, head) score entry actually computed (kept tiles, valid rows/cols)."""
     if mask is None:
@@ -85,6 +89,7 @@ def run_workload(cfg, warmup, steps):
     fill = -(-(cfg.anchor_frames + cfg.window_frames) // F)
     n_pool = max(cfg.steps if cfg.steps <= 8 else fill + 2, fill + 1)
     t0 = time.time()
+    log(f"{cfg.name}: drawing {n_pool} steps of inputs")
     pool = prepare(cfg, n_pool)
     cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, cfg.window_frames, cfg.anchor_frames)
     # key counts per pool step follow the window bookkeeping of the library itself
@@ -96,6 +101,7 @@ def run_workload(cfg, warmup, steps):
     cache.reset()
     attach_masks(cfg, pool, n_keys)
     prep_s = time.time() - t0
+    log(f"{cfg.name}: inputs ready in {prep_s:.1f} s; warm-up")
 
     out = torch.empty_like(pool[0]["q"])
     steady = list(range(fill, n_pool)) or [n_pool - 1]
@@ -118,6 +124,7 @@ def run_workload(cfg, warmup, steps):
     torch.cuda.synchronize()
     assert cache.window().n_keys == steady_keys(cfg)
 
+    log(f"{cfg.name}: timing {steps} steps")
     seq = [steady[i % len(steady)] for i in range(steps)]
     flops = [executed_flops(cfg.q_tokens, steady_keys(cfg), cfg.n_q_heads, cfg.head_dim, pool[s]["mask_np"])
              for s in seq]
@@ -187,6 +194,7 @@ def cpu_baseline(cfg, pool_step, budget_s=12.0):
                                 None if mask is None else mask[:, t:t + 1, :]) for t in tiles)
         return dt, fl
 
+    log(f"cpu baseline: oracle on {cfg.name} step {pool_step}")
     t1, _ = timed([0])                                   # calibration: one query tile
     n = int(max(1, min(n_qt - 1, budget_s / max(t1, 1e-3))))
     tiles = list(range(1, 1 + n)) if n_qt > 1 else [0]

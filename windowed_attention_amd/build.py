@@ -22,6 +22,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # mfma results in VGPRs: the online-softmax rescale of the accumulators is a VALU op, and
+    # AGPR accumulators would be copied to VGPRs and back on every key tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

@@ -61,45 +61,65 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendParams p) {
 // ---------------------------------------------------------------------------
 // Attention.
 //
-// Work-group: 4 waves, 128 (query, head) rows.  Each wave owns 32 queries of
-// one query head.  Per key tile of 128 keys:
-//   S^T = K . Q^T   mfma 32x32x16 bf16: A = K rows from LDS, B = Q^T in registers
-//   online softmax  fp32, per query = per lane (query = lane % 32), the two
-//                   lane halves hold different keys of the same query
-//   O^T += V^T . P^T  mfma 32x32x16: A = V^T from LDS (stored transposed),
-//                   B = P^T straight from the S^T registers.
-// K rows are fed to the S^T mfma in a permuted order (rowperm) so that the
-// 16 keys of each S^T register group that a lane half holds are 8
-// consecutive keys: P^T then serves as the B operand of the PV mfma with no
-// data movement.
+// Work-group: 4 waves, 128 (query, head) rows = 4 row blocks of 32 queries of
+// one query head.  The K and V tiles of 128 keys come straight from global
+// memory into LDS (global_load_lds, 16 bytes per lane, no register staging),
+// double-buffered so that tile i+1 streams in while tile i is computed.
+// Wave w computes row blocks 2*(w&1), 2*(w&1)+1 (64 rows) against key half
+// w>>1 (64 keys) of every tile, so each K/V fragment read from LDS feeds two
+// mfma: per FLOP a wave reads half the LDS bytes of a 32-row x 128-key wave.
+// The two key halves of a row keep separate softmax statistics and are
+// merged once at the end.
+//
+//   S^T = K . Q^T     mfma 32x32x16 bf16: A = K rows (LDS), B = Q^T (registers)
+//   online softmax    fp32 per query (= per lane % 32); rescaling of the
+//                     running output is skipped until the running max grows
+//                     by more than 2^8 (exact: only the reference point moves)
+//   O^T += V^T . P^T  mfma 32x32x16: A = V^T read from the row-major V tile
+//                     with the gfx950 LDS transpose read, B = P^T from the
+//                     S^T registers
+// K rows are fed to the S^T mfma in a permuted order (rowperm) so that each
+// lane half's 8 keys of an S^T accumulator group are 8 consecutive keys:
+// P^T then is the B operand of the PV mfma with no data movement.
 //
 // mfma_f32_32x32x16_bf16 operand layout (lane l, element e):
 //   A[m = l % 32][k = 8*(l / 32) + e],  B[k = 8*(l / 32) + e][n = l % 32],
 //   C[m = 8*(j / 4) + 4*(l / 32) + j % 4][n = l % 32] in accumulator j.
+// ds_read_b64_tr_b16, per group of 16 lanes: lane i receives element i % 4
+// of the 4-element (8-byte) reads of lanes 4r + i / 4, r = 0..3.
+//
+// LDS tiles are row-major (one key per row, head_dim contiguous) with the
+// 16-byte chunk c of row r stored at chunk position c ^ (r % chunks_per_row),
+// which keeps the strided fragment reads free of bank conflicts.
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define UF_LDS __attribute__((address_space(3)))
+#define UF_GLOBAL __attribute__((address_space(1)))
 
 __device__ inline int rowperm(int m) {  // swap bits 2 and 3 (an involution)
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-template <int D>
-struct AttnSmem {
-  static constexpr int kStr = D + 8;        // K row stride (elements), +16 B against bank conflicts
-  static constexpr int vStr = kTile + 8;    // V^T row stride (one row per d)
-  __bf16 k[kTile * kStr];
-  __bf16 vt[D * vStr];
-};
+__device__ inline void load_lds16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const UF_GLOBAL void*)src, (UF_LDS void*)lds_dst, 16, 0, 0);
+}
 
 template <int D>
 __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
-  constexpr int NC = D / 16;  // 16-wide d chunks of the S^T mfma
-  constexpr int ND = D / 32;  // 32-row d blocks of O^T
-  constexpr int kStr = AttnSmem<D>::kStr;
-  constexpr int vStr = AttnSmem<D>::vStr;
-  __shared__ AttnSmem<D> sm;
+  constexpr int NC = D / 16;            // 16-wide d chunks of the S^T mfma
+  constexpr int ND = D / 32;            // 32-row d blocks of O^T
+  constexpr int CPR = D / 8;            // 16-byte chunks per LDS row
+  constexpr int RB = D * 2;             // bytes per LDS row
+  constexpr int TILE_B = kTile * RB;    // bytes per K (or V) tile
+  constexpr int RPI = 64 / CPR;         // rows written by one wave-wide 16-byte load
+  constexpr int NLD = kTile / RPI / 4;  // such loads per wave, per tensor and tile
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
+  const int kh = wave >> 1;   // key half of each tile
+  const int pair = wave & 1;  // row blocks 2*pair and 2*pair+1
 
   // ---- work item
   const int item = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -108,32 +128,39 @@ __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
   const int split = rest % p.splits;
   const int hgrp = rest / p.splits;
   const int waves_per_head = 4 / p.heads_per_wg;
-  const int qpw = kTile / p.heads_per_wg;                     // queries per work-group
-  const int head = hgrp * p.heads_per_wg + wave / waves_per_head;
-  const int q0 = qblk * qpw;
-  const int qi = q0 + (wave % waves_per_head) * 32 + l32;     // this lane's query row
-  const int kvh = head / p.group;
-  const int q_tile = q0 / kTile;                              // block-mask row
+  const int q0 = qblk * (kTile / p.heads_per_wg);
+  const int kvh = (hgrp * p.heads_per_wg) / p.group;
+  const int q_tile = q0 / kTile;  // block-mask row
+  int head[2], qi[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int rb = 2 * pair + qb;
+    head[qb] = hgrp * p.heads_per_wg + rb / waves_per_head;
+    qi[qb] = q0 + (rb % waves_per_head) * 32 + l32;
+  }
 
-  // ---- Q^T fragments (B operand), kept in registers for the whole key range
-  bf16x8 qf[NC];
-  {
-    const bool ok = qi < p.n_q;
-    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(ok ? qi : 0) * p.q_stride_tok +
-                       (int64_t)head * p.q_stride_head + 8 * half;
+  // ---- Q^T fragments (B operand), in registers for the whole key range
+  bf16x8 qf[2][NC];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const bool ok = qi[qb] < p.n_q;
+    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(ok ? qi[qb] : 0) * p.q_stride_tok +
+                       (int64_t)head[qb] * p.q_stride_head + 8 * half;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
       if (!ok) x = bf16x8{};
-      qf[c] = x;
+      qf[qb][c] = x;
     }
   }
 
-  f32x16 o[ND];
+  f32x16 o[2][ND];
 #pragma unroll
-  for (int i = 0; i < ND; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY;  // running max of raw scores for this lane's query
-  float l_run = 0.f;        // this lane half's partial sum of probabilities
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < ND; ++i) o[qb][i] = f32x16{};
+  float m_run[2] = {-INFINITY, -INFINITY};  // reference max (raw score units) per query
+  float l_run[2] = {0.f, 0.f};              // this lane half's sum of probabilities
   const float c2 = p.scale_log2;
 
   const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)kvh * p.kv_head_stride;
@@ -150,148 +177,246 @@ __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
   const int nkt = (p.n_k + kTile - 1) / kTile;
   const int kt_lo = (int)(((int64_t)split * nkt) / p.splits);
   const int kt_hi = (int)(((int64_t)(split + 1) * nkt) / p.splits);
-
   const uint8_t* mrow = nullptr;
   if (p.mask) {
-    const int mh = p.mask_heads == 1 ? 0 : head;  // heads_per_wg > 1 only with a shared mask
+    const int mh = p.mask_heads == 1 ? 0 : head[0];  // heads_per_wg > 1 only with a shared mask
     mrow = p.mask + mh * p.mask_stride_head + (int64_t)q_tile * p.mask_stride_q;
   }
 
-  for (int w0 = kt_lo; w0 < kt_hi; w0 += 64) {
-    uint64_t bits;
-    if (mrow) {
-      const int kt = w0 + lane;
-      const bool keep = kt < kt_hi && mrow[kt] != 0;
-      bits = __ballot(keep);
-    } else {
-      const int n = min(64, kt_hi - w0);
-      bits = n == 64 ? ~0ull : ((1ull << n) - 1ull);
+  // kept key tiles in ascending order: 64 at a time from a wave ballot over the mask row
+  int w0 = kt_lo - 64;
+  uint64_t bits = 0;
+  auto next_tile = [&]() -> int {
+    while (bits == 0) {
+      w0 += 64;
+      if (w0 >= kt_hi) return -1;
+      if (mrow) {
+        const int kt = w0 + lane;
+        bits = __ballot(kt < kt_hi && mrow[kt] != 0);
+      } else {
+        const int n = min(64, kt_hi - w0);
+        bits = n == 64 ? ~0ull : ((1ull << n) - 1ull);
+      }
     }
-    while (bits) {
-      const int kt = w0 + __builtin_ctzll(bits);
-      bits &= bits - 1;
-      const int j0 = kt * kTile;
-      const int nvalid = min(kTile, p.n_k - j0);
+    const int kt = w0 + __builtin_ctzll(bits);
+    bits &= bits - 1;
+    return kt;
+  };
 
-      __syncthreads();  // previous tile's LDS reads are done
-      // ---- K tile -> LDS, row-major [key][d]
-      {
-        constexpr int cpr = D / 8;             // 16-byte chunks per row
-        constexpr int rpp = kThreads / cpr;    // rows per pass
-        const int c8 = tid % cpr;
+  // K and V of tile kt -> LDS buffer b (asynchronous; completion via vmcnt).
+  // Lane element offsets for a tile whose 128 keys are 128 consecutive storage
+  // rows (every full tile that does not cross the anchor/ring boundary or
+  // the ring's wrap): the tile is then one scalar base plus these offsets.
+  int lane_off[NLD];
 #pragma unroll
-        for (int r = tid / cpr; r < kTile; r += rpp) {
-          uint4 val = make_uint4(0, 0, 0, 0);
-          if (r < nvalid) val = *reinterpret_cast<const uint4*>(kbase + (int64_t)key_row(j0 + r) * D + c8 * 8);
-          *reinterpret_cast<uint4*>(&sm.k[r * kStr + c8 * 8]) = val;
-        }
+  for (int i = 0; i < NLD; ++i) {
+    const int row = (wave * NLD + i) * RPI + lane / CPR;
+    lane_off[i] = row * D + ((lane % CPR) ^ (row % CPR)) * 8;
+  }
+  auto issue = [&](int kt, int b) {
+    const int j0 = kt * kTile;
+    const int nvalid = min(kTile, p.n_k - j0);
+    char* kd = smem + (2 * b) * TILE_B;
+    char* vd = kd + TILE_B;
+    int r0 = -1;  // first storage row when the tile is contiguous
+    if (nvalid == kTile) {
+      if (j0 + kTile <= p.anchor_keys) {
+        r0 = j0;
+      } else if (j0 >= p.anchor_keys) {
+        int r = j0 - p.anchor_keys + p.ring_rot;
+        if (r >= p.ring_cap) r -= p.ring_cap;
+        if (r + kTile <= p.ring_cap) r0 = p.ring_base + r;
       }
-      // ---- V tile -> LDS, transposed [d][key]
-      {
-        const int r = tid % kTile;            // key within the tile
-        const bool ok = r < nvalid;
-        const __bf16* vrow = vbase + (int64_t)(ok ? key_row(j0 + r) : 0) * D;
+    }
+    if (r0 >= 0) {
+      const __bf16* kt_base = kbase + (int64_t)r0 * D;
+      const __bf16* vt_base = vbase + (int64_t)r0 * D;
 #pragma unroll
-        for (int c8 = tid / kTile; c8 < D / 8; c8 += kThreads / kTile) {
-          bf16x8 val = *reinterpret_cast<const bf16x8*>(vrow + c8 * 8);
-          if (!ok) val = bf16x8{};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sm.vt[(c8 * 8 + e) * vStr + r] = val[e];
-        }
+      for (int i = 0; i < NLD; ++i) {
+        load_lds16(kt_base + lane_off[i], kd + (wave * NLD + i) * 1024);
+        load_lds16(vt_base + lane_off[i], vd + (wave * NLD + i) * 1024);
       }
-      __syncthreads();
+    } else {  // partial tile, or one that straddles the anchor/ring boundary or the wrap
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int ins = wave * NLD + i;
+        const int row = ins * RPI + lane / CPR;
+        const int chunk = (lane % CPR) ^ (row % CPR);
+        const int64_t off = (int64_t)key_row(j0 + min(row, nvalid - 1)) * D + chunk * 8;
+        load_lds16(kbase + off, kd + ins * 1024);
+        load_lds16(vbase + off, vd + ins * 1024);
+      }
+    }
+  };
 
-      // ---- S^T = K Q^T for 4 blocks of 32 keys
-      f32x16 s[4];
+  // lane constants of the V^T transpose reads
+  const int tr_r = (lane & 15) >> 2;                        // key within a group of 4
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // d offset within a 32-row d block
+
+  int kt = next_tile();
+  int buf = 0;
+  if (kt >= 0) issue(kt, 0);
+  while (kt >= 0) {
+    const int kt_next = next_tile();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile kt is in LDS for every wave; buffer buf^1 is free
+    if (kt_next >= 0) issue(kt_next, buf ^ 1);
+
+    const int nvalid = min(kTile, p.n_k - kt * kTile);
+    if (64 * kh < nvalid) {  // this wave's key half holds at least one key
+      const char* kl = smem + (2 * buf) * TILE_B;
+      const char* vl = kl + TILE_B;
+
+      // ---- S^T = K Q^T: 2 blocks of 32 keys x 2 blocks of 32 queries
+      f32x16 s[2][2];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = f32x16{};
-        const __bf16* krow = &sm.k[(32 * kb + rowperm(l32)) * kStr + 8 * half];
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = 64 * kh + 32 * kb + rowperm(l32);
+        const char* kr = kl + row * RB;
+        const int sw = row % CPR;
+        s[kb][0] = f32x16{};
+        s[kb][1] = f32x16{};
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * c);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + (((2 * c + half) ^ sw) << 4));
+          s[kb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][c], s[kb][0], 0, 0, 0);
+          s[kb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][c], s[kb][1], 0, 0, 0);
         }
       }
-      // S^T accumulator j of block kb holds key 32*kb + 16*(j/8) + 8*half + j%8
+      // accumulator j of key block kb holds key 64*kh + 32*kb + 16*(j/8) + 8*half + j%8
       if (nvalid < kTile) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j)
-            if (32 * kb + 16 * (j / 8) + 8 * half + (j % 8) >= nvalid) s[kb][j] = -INFINITY;
+            if (64 * kh + 32 * kb + 16 * (j / 8) + 8 * half + (j % 8) >= nvalid) {
+              s[kb][0][j] = -INFINITY;
+              s[kb][1][j] = -INFINITY;
+            }
       }
 
-      // ---- online softmax (fp32)
-      float mx = s[0][0];
+      // ---- online softmax (fp32), lazy rescaling
+      bf16x8 pb[2][4];  // P^T chunk t holds keys 64*kh + 16t + 8*half + e
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int qb = 0; qb < 2; ++qb) {
+        float mx = s[0][qb][0];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-      m_run = m_new;
-      l_run *= alpha;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < ND; ++i) o[i] *= alpha;
-      const float mc = m_new * c2;
-
-      bf16x8 pb[8];  // P^T for 8 chunks of 16 keys: chunk t holds keys 16t + 8*half + e
+          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][qb][j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[qb], mx);
+        const bool need = (m_new - m_run[qb]) * c2 > 8.f;
+        if (__ballot(need)) {
+          const float alpha = need ? __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c2) : 1.f;
+          if (need) m_run[qb] = m_new;
+          l_run[qb] *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          f32x8 pv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = __builtin_amdgcn_exp2f(s[kb][8 * hf + e] * c2 - mc);
-            l_run += x;
-            pv[e] = x;
-          }
-          pb[2 * kb + hf] = __builtin_convertvector(pv, bf16x8);
+          for (int i = 0; i < ND; ++i) o[qb][i] *= alpha;
         }
+        const float mc = m_run[qb] * c2;
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            f32x8 pv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * hf + e], c2, -mc));
+              lsum += x;
+              pv[e] = x;
+            }
+            pb[qb][2 * kb + hf] = __builtin_convertvector(pv, bf16x8);
+          }
+        l_run[qb] += lsum;
       }
 
       // ---- O^T += V^T P^T
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        const __bf16* vrow = &sm.vt[(32 * db + l32) * vStr + 8 * half];
+        const int col = 32 * db + tr_col;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + 16 * t);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], o[db], 0, 0, 0);
+        for (int t = 0; t < 4; ++t) {
+          i16x4 v[2];
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) {
+            const int key = 64 * kh + 16 * t + 8 * half + 4 * sub + tr_r;
+            const char* addr = vl + key * RB + ((((col >> 3) ^ (key % CPR)) << 4) | ((col & 7) << 1));
+            v[sub] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((UF_LDS i16x4*)addr);
+          }
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][t], o[0][db], 0, 0, 0);
+          o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][t], o[1][db], 0, 0, 0);
         }
       }
     }
+    kt = kt_next;
+    buf ^= 1;
   }
 
-  // ---- epilogue.  O^T accumulator j of d-block db holds d = 32*db + 8*(j/4) + 4*half + j%4.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qi >= p.n_q) return;
-  if (p.splits == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)qi * p.o_stride_tok + (int64_t)head * p.o_stride_head;
+  // ---- merge the two key halves of every row (LDS exchange), then write
+  float l_tot[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) l_tot[qb] = l_run[qb] + __shfl_xor(l_run[qb], 32);
+  __syncthreads();  // every wave is done with the tile buffers
+  float* xo = reinterpret_cast<float*>(smem);   // [pair][qb][ND][16][64]
+  float* xm = xo + 2 * 2 * ND * 16 * 64;         // [pair][qb][2][64]
+  if (kh == 1) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) xo[(((pair * 2 + qb) * ND + db) * 16 + j) * 64 + lane] = o[qb][db][j];
+      xm[((pair * 2 + qb) * 2 + 0) * 64 + lane] = m_run[qb];
+      xm[((pair * 2 + qb) * 2 + 1) * 64 + lane] = l_tot[qb];
+    }
+  }
+  __syncthreads();
+  if (kh == 1) return;
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float mb = xm[((pair * 2 + qb) * 2 + 0) * 64 + lane];
+    const float lb = xm[((pair * 2 + qb) * 2 + 1) * 64 + lane];
+    const float M = fmaxf(m_run[qb], mb);
+    const float wa = m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run[qb] - M) * c2);
+    const float wb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mb - M) * c2);
+    const float l = l_tot[qb] * wa + lb * wb;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 x = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
-        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g + 4 * half) = __builtin_convertvector(x, bf16x4);
-      }
-  } else {
-    const int64_t row = ((int64_t)split * p.n_q + qi) * p.n_q_heads + head;
-    float* wo = p.ws_o + row * D;
+      for (int j = 0; j < 16; ++j)
+        o[qb][db][j] = o[qb][db][j] * wa + xo[(((pair * 2 + qb) * ND + db) * 16 + j) * 64 + lane] * wb;
+    if (qi[qb] >= p.n_q) continue;
+    // O^T accumulator j of d block db holds d = 32*db + 8*(j/4) + 4*half + j%4
+    if (p.splits == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)qi[qb] * p.o_stride_tok +
+                   (int64_t)head[qb] * p.o_stride_head;
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
+      for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 x = {o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
-        *reinterpret_cast<f32x4*>(wo + 32 * db + 8 * g + 4 * half) = x;
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x = {o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv, o[qb][db][4 * g + 2] * inv,
+                     o[qb][db][4 * g + 3] * inv};
+          *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g + 4 * half) = __builtin_convertvector(x, bf16x4);
+        }
+    } else {
+      const int64_t row = ((int64_t)split * p.n_q + qi[qb]) * p.n_q_heads + head[qb];
+      float* wo = p.ws_o + row * D;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x = {o[qb][db][4 * g], o[qb][db][4 * g + 1], o[qb][db][4 * g + 2], o[qb][db][4 * g + 3]};
+          *reinterpret_cast<f32x4*>(wo + 32 * db + 8 * g + 4 * half) = x;
+        }
+      if (half == 0) {
+        p.ws_ml[2 * row] = M * c2;  // -inf when this split saw no key
+        p.ws_ml[2 * row + 1] = l;
       }
-    if (half == 0) {
-      p.ws_ml[2 * row] = m_run * c2;  // -inf when this split saw no key
-      p.ws_ml[2 * row + 1] = l_tot;
     }
   }
 }
