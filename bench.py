@@ -244,6 +244,9 @@ def main():
     ap.add_argument("--also", default="1k", help="comma-separated extra workloads reported under 'also' ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work in the CPU baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (3 times), a known-size kernel "
+                         "against which profiler byte counters are scaled")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -252,6 +255,15 @@ def main():
 
     import torch
     torch.cuda.init()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)  # reads and writes n * 4 bytes
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {args.copy_calibration_mib} MiB")
+        del src, dst
     cfg = {c.name: c for c in CONFIGS}[args.workload]
     main_r = run_workload(cfg, args.warmup, args.steps)
     also = {}

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "uf_internal.h"
 
 namespace uf {
@@ -89,8 +91,7 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendParams p) {
 // of the 4-element (8-byte) reads of lanes 4r + i / 4, r = 0..3.
 //
 // LDS tiles are row-major (one key per row, head_dim contiguous) with the
-// 16-byte chunk c of row r stored at chunk position c ^ (r % chunks_per_row),
-// which keeps the strided fragment reads free of bank conflicts.
+// 16-byte chunks of every row permuted by an XOR swizzle (swz below).
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define UF_LDS __attribute__((address_space(3)))
@@ -104,6 +105,22 @@ __device__ inline void load_lds16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds((const UF_GLOBAL void*)src, (UF_LDS void*)lds_dst, 16, 0, 0);
 }
 
+// Chunk swizzle of LDS row r: its 16-byte chunk c is stored at position
+// c ^ swz(r).  Chosen (exhaustively over linear maps of r mod 16) so that
+// both the row-strided K reads (16 B per lane) and the transpose reads of V
+// (8 B per lane) hit distinct banks with 32 or with 64 four-byte banks.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  const int r = row & 15;
+  if constexpr (D == 128)
+    return ((r & 1) ? 4 : 0) ^ ((r & 2) ? 10 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 3 : 0);
+  else
+    return ((r & 1) ? 2 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 3 : 0);
+}
+
+template <int B>
+using Buf = std::integral_constant<int, B>;
+
 template <int D>
 __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
   constexpr int NC = D / 16;            // 16-wide d chunks of the S^T mfma
@@ -113,6 +130,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
   constexpr int TILE_B = kTile * RB;    // bytes per K (or V) tile
   constexpr int RPI = 64 / CPR;         // rows written by one wave-wide 16-byte load
   constexpr int NLD = kTile / RPI / 4;  // such loads per wave, per tensor and tile
+  constexpr int V_REGION = 2 * TILE_B;  // LDS: [K buf 0][K buf 1][V buf 0][V buf 1]
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_B];
 
   const int tid = threadIdx.x;
@@ -207,17 +225,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
   // Lane element offsets for a tile whose 128 keys are 128 consecutive storage
   // rows (every full tile that does not cross the anchor/ring boundary or
   // the ring's wrap): the tile is then one scalar base plus these offsets.
-  int lane_off[NLD];
+  uint32_t lane_off[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int row = (wave * NLD + i) * RPI + lane / CPR;
-    lane_off[i] = row * D + ((lane % CPR) ^ (row % CPR)) * 8;
+    lane_off[i] = row * D + ((lane % CPR) ^ swz<D>(row)) * 8;
   }
   auto issue = [&](int kt, int b) {
     const int j0 = kt * kTile;
     const int nvalid = min(kTile, p.n_k - j0);
-    char* kd = smem + (2 * b) * TILE_B;
-    char* vd = kd + TILE_B;
+    char* kd = smem + b * TILE_B + wave * NLD * 1024;
+    char* vd = kd + V_REGION;
     int r0 = -1;  // first storage row when the tile is contiguous
     if (nvalid == kTile) {
       if (j0 + kTile <= p.anchor_keys) {
@@ -233,126 +251,144 @@ __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
       const __bf16* vt_base = vbase + (int64_t)r0 * D;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        load_lds16(kt_base + lane_off[i], kd + (wave * NLD + i) * 1024);
-        load_lds16(vt_base + lane_off[i], vd + (wave * NLD + i) * 1024);
+        load_lds16(kt_base + lane_off[i], kd + i * 1024);
+        load_lds16(vt_base + lane_off[i], vd + i * 1024);
       }
     } else {  // partial tile, or one that straddles the anchor/ring boundary or the wrap
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const int ins = wave * NLD + i;
-        const int row = ins * RPI + lane / CPR;
-        const int chunk = (lane % CPR) ^ (row % CPR);
+        const int row = (wave * NLD + i) * RPI + lane / CPR;
+        const int chunk = (lane % CPR) ^ swz<D>(row);
         const int64_t off = (int64_t)key_row(j0 + min(row, nvalid - 1)) * D + chunk * 8;
-        load_lds16(kbase + off, kd + ins * 1024);
-        load_lds16(vbase + off, vd + ins * 1024);
+        load_lds16(kbase + off, kd + i * 1024);
+        load_lds16(vbase + off, vd + i * 1024);
       }
     }
   };
 
-  // lane constants of the V^T transpose reads
-  const int tr_r = (lane & 15) >> 2;                        // key within a group of 4
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // d offset within a 32-row d block
+  // Per-lane LDS byte offsets of the fragment reads.  Every other term of an
+  // address (buffer, key block, key chunk) is a multiple of 16 rows, leaves
+  // the swizzle unchanged and goes into the instruction's immediate offset.
+  uint32_t koff[NC];  // K rows for S^T: row 64*kh + 32*kb + rowperm(l32), chunk 2c + half
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int r = rowperm(l32);
+    koff[c] = (64 * kh + r) * RB + (((2 * c + half) ^ swz<D>(r)) << 4);
+  }
+  uint32_t voff[ND][2];  // V rows for the transpose reads: key 64*kh + 16t + 8*half + 4*sub + (lane&15)/4
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int key = 8 * half + 4 * sub + ((lane & 15) >> 2);
+      const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      voff[db][sub] = V_REGION + (64 * kh + key) * RB + ((((col >> 3) ^ swz<D>(key)) << 4) | ((col & 7) << 1));
+    }
 
-  int kt = next_tile();
-  int buf = 0;
-  if (kt >= 0) issue(kt, 0);
-  while (kt >= 0) {
-    const int kt_next = next_tile();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile kt is in LDS for every wave; buffer buf^1 is free
-    if (kt_next >= 0) issue(kt_next, buf ^ 1);
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    const int nvalid = min(kTile, p.n_k - kt * kTile);
-    if (64 * kh < nvalid) {  // this wave's key half holds at least one key
-      const char* kl = smem + (2 * buf) * TILE_B;
-      const char* vl = kl + TILE_B;
+  // one tile held in LDS buffer B
+  auto compute = [&](auto buf, int nvalid) {
+    constexpr int B = decltype(buf)::value;
+    if (64 * kh >= nvalid) return;  // this wave's key half is empty
+    const char* lds = smem + B * TILE_B;
 
-      // ---- S^T = K Q^T: 2 blocks of 32 keys x 2 blocks of 32 queries
-      f32x16 s[2][2];
+    // ---- S^T = K Q^T: 2 blocks of 32 keys x 2 blocks of 32 queries
+    f32x16 s[2][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = 64 * kh + 32 * kb + rowperm(l32);
-        const char* kr = kl + row * RB;
-        const int sw = row % CPR;
-        s[kb][0] = f32x16{};
-        s[kb][1] = f32x16{};
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb][0] = f32x16{};
+      s[kb][1] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + (((2 * c + half) ^ sw) << 4));
-          s[kb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][c], s[kb][0], 0, 0, 0);
-          s[kb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][c], s[kb][1], 0, 0, 0);
-        }
-      }
-      // accumulator j of key block kb holds key 64*kh + 32*kb + 16*(j/8) + 8*half + j%8
-      if (nvalid < kTile) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (64 * kh + 32 * kb + 16 * (j / 8) + 8 * half + (j % 8) >= nvalid) {
-              s[kb][0][j] = -INFINITY;
-              s[kb][1][j] = -INFINITY;
-            }
-      }
-
-      // ---- online softmax (fp32), lazy rescaling
-      bf16x8 pb[2][4];  // P^T chunk t holds keys 64*kh + 16t + 8*half + e
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float mx = s[0][qb][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][qb][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[qb], mx);
-        const bool need = (m_new - m_run[qb]) * c2 > 8.f;
-        if (__ballot(need)) {
-          const float alpha = need ? __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c2) : 1.f;
-          if (need) m_run[qb] = m_new;
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int i = 0; i < ND; ++i) o[qb][i] *= alpha;
-        }
-        const float mc = m_run[qb] * c2;
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            f32x8 pv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * hf + e], c2, -mc));
-              lsum += x;
-              pv[e] = x;
-            }
-            pb[qb][2 * kb + hf] = __builtin_convertvector(pv, bf16x8);
-          }
-        l_run[qb] += lsum;
-      }
-
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const int col = 32 * db + tr_col;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          i16x4 v[2];
-#pragma unroll
-          for (int sub = 0; sub < 2; ++sub) {
-            const int key = 64 * kh + 16 * t + 8 * half + 4 * sub + tr_r;
-            const char* addr = vl + key * RB + ((((col >> 3) ^ (key % CPR)) << 4) | ((col & 7) << 1));
-            v[sub] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((UF_LDS i16x4*)addr);
-          }
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
-          o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][t], o[0][db], 0, 0, 0);
-          o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][t], o[1][db], 0, 0, 0);
-        }
+      for (int c = 0; c < NC; ++c) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + koff[c] + 32 * kb * RB);
+        s[kb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][c], s[kb][0], 0, 0, 0);
+        s[kb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][c], s[kb][1], 0, 0, 0);
       }
     }
-    kt = kt_next;
-    buf ^= 1;
+    // accumulator j of key block kb holds key 64*kh + 32*kb + 16*(j/8) + 8*half + j%8
+    if (nvalid < kTile) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (64 * kh + 32 * kb + 16 * (j / 8) + 8 * half + (j % 8) >= nvalid) {
+            s[kb][0][j] = -INFINITY;
+            s[kb][1][j] = -INFINITY;
+          }
+    }
+
+    // ---- online softmax (fp32), lazy rescaling; row sums of the bf16 probabilities
+    bf16x8 pb[2][4];  // P^T chunk t holds keys 64*kh + 16t + 8*half + e
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = s[0][qb][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][qb][j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[qb], mx);
+      const bool need = (m_new - m_run[qb]) * c2 > 8.f;
+      if (__ballot(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c2) : 1.f;
+        if (need) m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < ND; ++i) o[qb][i] *= alpha;
+      }
+      const float mc = m_run[qb] * c2;
+      float lsum = l_run[qb];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          f32x8 pv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * hf + e], c2, -mc));
+          const bf16x8 pk = __builtin_convertvector(pv, bf16x8);
+          pb[qb][2 * kb + hf] = pk;
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 0, 1), ones, lsum, false);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 2, 3), ones, lsum, false);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 4, 5), ones, lsum, false);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 6, 7), ones, lsum, false);
+        }
+      l_run[qb] = lsum;
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (UF_LDS i16x4*)(lds + voff[db][0] + 16 * t * RB));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (UF_LDS i16x4*)(lds + voff[db][1] + 16 * t * RB));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][t], o[0][db], 0, 0, 0);
+        o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][t], o[1][db], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- main loop, unrolled by two so that the LDS buffer is a compile-time constant
+  int kt = next_tile();
+  if (kt >= 0) issue(kt, 0);
+  while (kt >= 0) {
+    const int kt1 = next_tile();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile kt is in buffer 0 for every wave; buffer 1 is free
+    if (kt1 >= 0) issue(kt1, 1);
+    compute(Buf<0>{}, min(kTile, p.n_k - kt * kTile));
+    if (kt1 < 0) break;
+    const int kt2 = next_tile();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile kt1 is in buffer 1; buffer 0 is free
+    if (kt2 >= 0) issue(kt2, 0);
+    compute(Buf<1>{}, min(kTile, p.n_k - kt1 * kTile));
+    kt = kt2;
   }
 
   // ---- merge the two key halves of every row (LDS exchange), then write
