@@ -63,15 +63,15 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendParams p) {
 // ---------------------------------------------------------------------------
 // Attention.
 //
-// Work-group: 4 waves, 128 (query, head) rows = 4 row blocks of 32 queries of
-// one query head.  The K and V tiles of 128 keys come straight from global
-// memory into LDS (global_load_lds, 16 bytes per lane, no register staging),
-// double-buffered so that tile i+1 streams in while tile i is computed.
-// Wave w computes row blocks 2*(w&1), 2*(w&1)+1 (64 rows) against key half
-// w>>1 (64 keys) of every tile, so each K/V fragment read from LDS feeds two
-// mfma: per FLOP a wave reads half the LDS bytes of a 32-row x 128-key wave.
-// The two key halves of a row keep separate softmax statistics and are
-// merged once at the end.
+// Work-group: 8 waves (two per SIMD), 128 (query, head) rows = 4 row blocks
+// of 32 queries of one query head.  The K and V tiles of 128 keys come
+// straight from global memory into LDS (global_load_lds, 16 bytes per lane,
+// no register staging), double-buffered so that tile i+1 streams in while
+// tile i is computed.  Wave w computes row block w&3 against key half w>>2
+// (64 keys) of every tile; the two key halves of a row keep separate softmax
+// statistics and are merged once at the end.  Each wave stays within 256
+// registers, so two waves share a SIMD and one's softmax overlaps the
+// other's mfma.
 //
 //   S^T = K . Q^T     mfma 32x32x16 bf16: A = K rows (LDS), B = Q^T (registers)
 //   online softmax    fp32 per query (= per lane % 32); rescaling of the
@@ -121,23 +121,26 @@ __device__ __forceinline__ int swz(int row) {
 template <int B>
 using Buf = std::integral_constant<int, B>;
 
+constexpr int kAttnThreads = 512;  // 8 waves
+
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
+__global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
   constexpr int NC = D / 16;            // 16-wide d chunks of the S^T mfma
   constexpr int ND = D / 32;            // 32-row d blocks of O^T
   constexpr int CPR = D / 8;            // 16-byte chunks per LDS row
   constexpr int RB = D * 2;             // bytes per LDS row
   constexpr int TILE_B = kTile * RB;    // bytes per K (or V) tile
   constexpr int RPI = 64 / CPR;         // rows written by one wave-wide 16-byte load
-  constexpr int NLD = kTile / RPI / 4;  // such loads per wave, per tensor and tile
+  constexpr int NW = kAttnThreads / 64; // waves
+  constexpr int NLD = kTile / RPI / NW; // such loads per wave, per tensor and tile
   constexpr int V_REGION = 2 * TILE_B;  // LDS: [K buf 0][K buf 1][V buf 0][V buf 1]
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
-  const int kh = wave >> 1;   // key half of each tile
-  const int pair = wave & 1;  // row blocks 2*pair and 2*pair+1
+  const int kh = wave >> 2;  // key half of each tile
+  const int rb = wave & 3;   // row block
 
   // ---- work item
   const int item = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -149,36 +152,28 @@ __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
   const int q0 = qblk * (kTile / p.heads_per_wg);
   const int kvh = (hgrp * p.heads_per_wg) / p.group;
   const int q_tile = q0 / kTile;  // block-mask row
-  int head[2], qi[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int rb = 2 * pair + qb;
-    head[qb] = hgrp * p.heads_per_wg + rb / waves_per_head;
-    qi[qb] = q0 + (rb % waves_per_head) * 32 + l32;
-  }
+  const int head = hgrp * p.heads_per_wg + rb / waves_per_head;
+  const int qi = q0 + (rb % waves_per_head) * 32 + l32;
 
   // ---- Q^T fragments (B operand), in registers for the whole key range
-  bf16x8 qf[2][NC];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const bool ok = qi[qb] < p.n_q;
-    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(ok ? qi[qb] : 0) * p.q_stride_tok +
-                       (int64_t)head[qb] * p.q_stride_head + 8 * half;
+  bf16x8 qf[NC];
+  {
+    const bool ok = qi < p.n_q;
+    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(ok ? qi : 0) * p.q_stride_tok +
+                       (int64_t)head * p.q_stride_head + 8 * half;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
       if (!ok) x = bf16x8{};
-      qf[qb][c] = x;
+      qf[c] = x;
     }
   }
 
-  f32x16 o[2][ND];
+  f32x16 o[ND];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int i = 0; i < ND; ++i) o[qb][i] = f32x16{};
-  float m_run[2] = {-INFINITY, -INFINITY};  // reference max (raw score units) per query
-  float l_run[2] = {0.f, 0.f};              // this lane half's sum of probabilities
+  for (int i = 0; i < ND; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY;  // reference max (raw score units) of this lane's query
+  float l_run = 0.f;        // this lane half's sum of probabilities
   const float c2 = p.scale_log2;
 
   const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)kvh * p.kv_head_stride;
@@ -197,7 +192,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
   const int kt_hi = (int)(((int64_t)(split + 1) * nkt) / p.splits);
   const uint8_t* mrow = nullptr;
   if (p.mask) {
-    const int mh = p.mask_heads == 1 ? 0 : head[0];  // heads_per_wg > 1 only with a shared mask
+    const int mh = p.mask_heads == 1 ? 0 : head;  // heads_per_wg > 1 only with a shared mask
     mrow = p.mask + mh * p.mask_stride_head + (int64_t)q_tile * p.mask_stride_q;
   }
 
@@ -294,17 +289,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
     if (64 * kh >= nvalid) return;  // this wave's key half is empty
     const char* lds = smem + B * TILE_B;
 
-    // ---- S^T = K Q^T: 2 blocks of 32 keys x 2 blocks of 32 queries
-    f32x16 s[2][2];
+    // ---- S^T = K Q^T: 2 blocks of 32 keys x 32 queries
+    f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb][0] = f32x16{};
-      s[kb][1] = f32x16{};
+      s[kb] = f32x16{};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + koff[c] + 32 * kb * RB);
-        s[kb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][c], s[kb][0], 0, 0, 0);
-        s[kb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][c], s[kb][1], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
       }
     }
     // accumulator j of key block kb holds key 64*kh + 32*kb + 16*(j/8) + 8*half + j%8
@@ -313,49 +306,43 @@ __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (64 * kh + 32 * kb + 16 * (j / 8) + 8 * half + (j % 8) >= nvalid) {
-            s[kb][0][j] = -INFINITY;
-            s[kb][1][j] = -INFINITY;
-          }
+          if (64 * kh + 32 * kb + 16 * (j / 8) + 8 * half + (j % 8) >= nvalid) s[kb][j] = -INFINITY;
     }
 
     // ---- online softmax (fp32), lazy rescaling; row sums of the bf16 probabilities
-    bf16x8 pb[2][4];  // P^T chunk t holds keys 64*kh + 16t + 8*half + e
+    float mx = s[0][0];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = s[0][qb][0];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const bool need = (m_new - m_run) * c2 > 8.f;
+    if (__ballot(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c2) : 1.f;
+      if (need) m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][qb][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[qb], mx);
-      const bool need = (m_new - m_run[qb]) * c2 > 8.f;
-      if (__ballot(need)) {
-        const float alpha = need ? __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c2) : 1.f;
-        if (need) m_run[qb] = m_new;
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int i = 0; i < ND; ++i) o[qb][i] *= alpha;
-      }
-      const float mc = m_run[qb] * c2;
-      float lsum = l_run[qb];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          f32x8 pv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * hf + e], c2, -mc));
-          const bf16x8 pk = __builtin_convertvector(pv, bf16x8);
-          pb[qb][2 * kb + hf] = pk;
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 0, 1), ones, lsum, false);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 2, 3), ones, lsum, false);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 4, 5), ones, lsum, false);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 6, 7), ones, lsum, false);
-        }
-      l_run[qb] = lsum;
+      for (int i = 0; i < ND; ++i) o[i] *= alpha;
     }
+    const float mc = m_run * c2;
+    bf16x8 pb[4];  // P^T chunk t holds keys 64*kh + 16t + 8*half + e
+    float lsum = l_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        f32x8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * hf + e], c2, -mc));
+        const bf16x8 pk = __builtin_convertvector(pv, bf16x8);
+        pb[2 * kb + hf] = pk;
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 0, 1), ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 2, 3), ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 4, 5), ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 6, 7), ones, lsum, false);
+      }
+    l_run = lsum;
 
     // ---- O^T += V^T P^T
 #pragma unroll
@@ -367,8 +354,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
         const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (UF_LDS i16x4*)(lds + voff[db][1] + 16 * t * RB));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][t], o[0][db], 0, 0, 0);
-        o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][t], o[1][db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], o[db], 0, 0, 0);
       }
     }
   };
@@ -392,67 +378,56 @@ __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnParams p) {
   }
 
   // ---- merge the two key halves of every row (LDS exchange), then write
-  float l_tot[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) l_tot[qb] = l_run[qb] + __shfl_xor(l_run[qb], 32);
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
   __syncthreads();  // every wave is done with the tile buffers
-  float* xo = reinterpret_cast<float*>(smem);   // [pair][qb][ND][16][64]
-  float* xm = xo + 2 * 2 * ND * 16 * 64;         // [pair][qb][2][64]
+  float* xo = reinterpret_cast<float*>(smem);   // [rb][ND][16][64]
+  float* xm = xo + 4 * ND * 16 * 64;             // [rb][2][64]
   if (kh == 1) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) xo[(((pair * 2 + qb) * ND + db) * 16 + j) * 64 + lane] = o[qb][db][j];
-      xm[((pair * 2 + qb) * 2 + 0) * 64 + lane] = m_run[qb];
-      xm[((pair * 2 + qb) * 2 + 1) * 64 + lane] = l_tot[qb];
-    }
+      for (int j = 0; j < 16; ++j) xo[((rb * ND + db) * 16 + j) * 64 + lane] = o[db][j];
+    xm[(rb * 2 + 0) * 64 + lane] = m_run;
+    xm[(rb * 2 + 1) * 64 + lane] = l_tot;
   }
   __syncthreads();
   if (kh == 1) return;
 
+  const float mb = xm[(rb * 2 + 0) * 64 + lane];
+  const float lb = xm[(rb * 2 + 1) * 64 + lane];
+  const float M = fmaxf(m_run, mb);
+  const float wa = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - M) * c2);
+  const float wb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mb - M) * c2);
+  const float l = l_tot * wa + lb * wb;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float mb = xm[((pair * 2 + qb) * 2 + 0) * 64 + lane];
-    const float lb = xm[((pair * 2 + qb) * 2 + 1) * 64 + lane];
-    const float M = fmaxf(m_run[qb], mb);
-    const float wa = m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run[qb] - M) * c2);
-    const float wb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mb - M) * c2);
-    const float l = l_tot[qb] * wa + lb * wb;
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[db][j] = o[db][j] * wa + xo[((rb * ND + db) * 16 + j) * 64 + lane] * wb;
+  if (qi >= p.n_q) return;
+  // O^T accumulator j of d block db holds d = 32*db + 8*(j/4) + 4*half + j%4
+  if (p.splits == 1) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)qi * p.o_stride_tok + (int64_t)head * p.o_stride_head;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        o[qb][db][j] = o[qb][db][j] * wa + xo[(((pair * 2 + qb) * ND + db) * 16 + j) * 64 + lane] * wb;
-    if (qi[qb] >= p.n_q) continue;
-    // O^T accumulator j of d block db holds d = 32*db + 8*(j/4) + 4*half + j%4
-    if (p.splits == 1) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)qi[qb] * p.o_stride_tok +
-                   (int64_t)head[qb] * p.o_stride_head;
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 x = {o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv, o[qb][db][4 * g + 2] * inv,
-                     o[qb][db][4 * g + 3] * inv};
-          *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g + 4 * half) = __builtin_convertvector(x, bf16x4);
-        }
-    } else {
-      const int64_t row = ((int64_t)split * p.n_q + qi[qb]) * p.n_q_heads + head[qb];
-      float* wo = p.ws_o + row * D;
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 x = {o[qb][db][4 * g], o[qb][db][4 * g + 1], o[qb][db][4 * g + 2], o[qb][db][4 * g + 3]};
-          *reinterpret_cast<f32x4*>(wo + 32 * db + 8 * g + 4 * half) = x;
-        }
-      if (half == 0) {
-        p.ws_ml[2 * row] = M * c2;  // -inf when this split saw no key
-        p.ws_ml[2 * row + 1] = l;
+      for (int g = 0; g < 4; ++g) {
+        f32x4 x = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g + 4 * half) = __builtin_convertvector(x, bf16x4);
       }
+  } else {
+    const int64_t row = ((int64_t)split * p.n_q + qi) * p.n_q_heads + head;
+    float* wo = p.ws_o + row * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 x = {o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(wo + 32 * db + 8 * g + 4 * half) = x;
+      }
+    if (half == 0) {
+      p.ws_ml[2 * row] = M * c2;  // -inf when this split saw no key
+      p.ws_ml[2 * row + 1] = l;
     }
   }
 }
@@ -501,9 +476,9 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
 hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t stream) {
   const int items = p.n_qblk * p.n_hgrp * p.splits;
   if (head_dim == 128)
-    hipLaunchKernelGGL(attn_kernel<128>, dim3(items), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(attn_kernel<128>, dim3(items), dim3(kAttnThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(attn_kernel<64>, dim3(items), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(attn_kernel<64>, dim3(items), dim3(kAttnThreads), 0, stream, p);
   return hipGetLastError();
 }
 
