@@ -337,8 +337,10 @@ uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mas
     if (v >= 1 && v <= kMaxSplits) splits = std::min(v, n_kt);
   }
   const int64_t rows = (int64_t)n_q * hq;
-  while (splits > 1 && ((int64_t)splits * rows * (d.head_dim + 2) * (int64_t)sizeof(float) > (int64_t)d.workspace_bytes))
-    --splits;
+  const auto fits = [&](int s) {
+    return s == 1 || (int64_t)s * rows * (d.head_dim + 2) * (int64_t)sizeof(float) <= (int64_t)d.workspace_bytes;
+  };
+  while (splits > 1 && !fits(splits)) --splits;
   if (items * splits >= kMaxIndex) return fail(UF_ERR_CAPACITY, "grid too large");
 
   uf::AttnParams p;

@@ -137,7 +137,8 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_B];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
   const int kh = wave >> 2;  // key half of each tile
   const int rb = wave & 3;   // row block
@@ -213,7 +214,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
     }
     const int kt = w0 + __builtin_ctzll(bits);
     bits &= bits - 1;
-    return kt;
+    return __builtin_amdgcn_readfirstlane(kt);
   };
 
   // K and V of tile kt -> LDS buffer b (asynchronous; completion via vmcnt).
