@@ -8,8 +8,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "uf_internal.h"
 
 namespace uf {
@@ -63,20 +61,19 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendParams p) {
 // ---------------------------------------------------------------------------
 // Attention.
 //
-// Work-group: 8 waves (two per SIMD), 128 (query, head) rows = 4 row blocks
-// of 32 queries of one query head.  The K and V tiles of 128 keys come
-// straight from global memory into LDS (global_load_lds, 16 bytes per lane,
-// no register staging), double-buffered so that tile i+1 streams in while
-// tile i is computed.  Wave w computes row block w&3 against key half w>>2
-// (64 keys) of every tile; the two key halves of a row keep separate softmax
-// statistics and are merged once at the end.  Each wave stays within 256
-// registers, so two waves share a SIMD and one's softmax overlaps the
-// other's mfma.
+// Work-group: 4 waves, 128 (query, head) rows = 4 row blocks of 32 queries
+// of one query head, one wave per row block; two work-groups share a CU.
+// Per kept key tile (128 keys) the work-group stages K and V straight from
+// global memory into LDS (global_load_lds, 16 bytes per lane, no register
+// staging) and every wave computes its 32 rows against all 128 keys.  The
+// LDS tile is single-buffered: while one work-group of a CU waits for its
+// next tile, the other computes.
 //
 //   S^T = K . Q^T     mfma 32x32x16 bf16: A = K rows (LDS), B = Q^T (registers)
 //   online softmax    fp32 per query (= per lane % 32); rescaling of the
 //                     running output is skipped until the running max grows
-//                     by more than 2^8 (exact: only the reference point moves)
+//                     by more than 2^8 (exact: only the reference point moves);
+//                     row sums of the bf16 probabilities with v_dot2
 //   O^T += V^T . P^T  mfma 32x32x16: A = V^T read from the row-major V tile
 //                     with the gfx950 LDS transpose read, B = P^T from the
 //                     S^T registers
@@ -118,13 +115,10 @@ __device__ __forceinline__ int swz(int row) {
     return ((r & 1) ? 2 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 3 : 0);
 }
 
-template <int B>
-using Buf = std::integral_constant<int, B>;
-
-constexpr int kAttnThreads = 512;  // 8 waves
+constexpr int kAttnThreads = 256;  // 4 waves; two work-groups per CU
 
 template <int D>
-__global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
+__global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
   constexpr int NC = D / 16;            // 16-wide d chunks of the S^T mfma
   constexpr int ND = D / 32;            // 32-row d blocks of O^T
   constexpr int CPR = D / 8;            // 16-byte chunks per LDS row
@@ -133,15 +127,13 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
   constexpr int RPI = 64 / CPR;         // rows written by one wave-wide 16-byte load
   constexpr int NW = kAttnThreads / 64; // waves
   constexpr int NLD = kTile / RPI / NW; // such loads per wave, per tensor and tile
-  constexpr int V_REGION = 2 * TILE_B;  // LDS: [K buf 0][K buf 1][V buf 0][V buf 1]
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_B];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_B];  // [K tile][V tile]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int kh = wave >> 2;  // key half of each tile
-  const int rb = wave & 3;   // row block
+  const int rb = wave;  // row block
 
   // ---- work item
   const int item = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -154,7 +146,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
   const int kvh = (hgrp * p.heads_per_wg) / p.group;
   const int q_tile = q0 / kTile;  // block-mask row
   const int head = hgrp * p.heads_per_wg + rb / waves_per_head;
-  const int qi = q0 + (rb % waves_per_head) * 32 + l32;
+  const int qi = q0 + (rb % waves_per_head) * 32 + l32;  // this lane's query row
 
   // ---- Q^T fragments (B operand), in registers for the whole key range
   bf16x8 qf[NC];
@@ -169,17 +161,14 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
       qf[c] = x;
     }
   }
-
   f32x16 o[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) o[i] = f32x16{};
   float m_run = -INFINITY;  // reference max (raw score units) of this lane's query
   float l_run = 0.f;        // this lane half's sum of probabilities
   const float c2 = p.scale_log2;
-
   const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)kvh * p.kv_head_stride;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)kvh * p.kv_head_stride;
-
   // storage row of logical key j
   auto key_row = [&](int j) -> int {
     if (j < p.anchor_keys) return j;
@@ -187,7 +176,6 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
     if (r >= p.ring_cap) r -= p.ring_cap;
     return p.ring_base + r;
   };
-
   const int nkt = (p.n_k + kTile - 1) / kTile;
   const int kt_lo = (int)(((int64_t)split * nkt) / p.splits);
   const int kt_hi = (int)(((int64_t)(split + 1) * nkt) / p.splits);
@@ -196,7 +184,6 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
     const int mh = p.mask_heads == 1 ? 0 : head;  // heads_per_wg > 1 only with a shared mask
     mrow = p.mask + mh * p.mask_stride_head + (int64_t)q_tile * p.mask_stride_q;
   }
-
   // kept key tiles in ascending order: 64 at a time from a wave ballot over the mask row
   int w0 = kt_lo - 64;
   uint64_t bits = 0;
@@ -214,11 +201,11 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
     }
     const int kt = w0 + __builtin_ctzll(bits);
     bits &= bits - 1;
-    return __builtin_amdgcn_readfirstlane(kt);
+    return __builtin_amdgcn_readfirstlane(kt);  // the same on every lane
   };
 
-  // K and V of tile kt -> LDS buffer b (asynchronous; completion via vmcnt).
-  // Lane element offsets for a tile whose 128 keys are 128 consecutive storage
+  // K and V of tile kt -> LDS (asynchronous; completion via vmcnt).  Lane
+  // element offsets for a tile whose 128 keys are 128 consecutive storage
   // rows (every full tile that does not cross the anchor/ring boundary or
   // the ring's wrap): the tile is then one scalar base plus these offsets.
   uint32_t lane_off[NLD];
@@ -227,12 +214,12 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
     const int row = (wave * NLD + i) * RPI + lane / CPR;
     lane_off[i] = row * D + ((lane % CPR) ^ swz<D>(row)) * 8;
   }
-  auto issue = [&](int kt, int b) {
+  auto issue = [&](int kt) {
     const int j0 = kt * kTile;
     const int nvalid = min(kTile, p.n_k - j0);
-    char* kd = smem + b * TILE_B + wave * NLD * 1024;
-    char* vd = kd + V_REGION;
-    int r0 = -1;  // first storage row when the tile is contiguous
+    char* kd = smem + wave * NLD * 1024;
+    char* vd = kd + TILE_B;
+    int r0 = -1;
     if (nvalid == kTile) {
       if (j0 + kTile <= p.anchor_keys) {
         r0 = j0;
@@ -261,64 +248,56 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
       }
     }
   };
-
   // Per-lane LDS byte offsets of the fragment reads.  Every other term of an
-  // address (buffer, key block, key chunk) is a multiple of 16 rows, leaves
-  // the swizzle unchanged and goes into the instruction's immediate offset.
-  uint32_t koff[NC];  // K rows for S^T: row 64*kh + 32*kb + rowperm(l32), chunk 2c + half
+  // address (key block, key chunk) is a multiple of 16 rows, leaves the
+  // swizzle unchanged and goes into the instruction's immediate offset.
+  uint32_t koff[NC];  // K rows for S^T: row 32*kb + rowperm(l32), chunk 2c + half
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int r = rowperm(l32);
-    koff[c] = (64 * kh + r) * RB + (((2 * c + half) ^ swz<D>(r)) << 4);
+    koff[c] = r * RB + (((2 * c + half) ^ swz<D>(r)) << 4);
   }
-  uint32_t voff[ND][2];  // V rows for the transpose reads: key 64*kh + 16t + 8*half + 4*sub + (lane&15)/4
+  uint32_t voff[ND][2];  // V rows for the transpose reads: key 16t + 8*half + 4*sub + (lane&15)/4
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int key = 8 * half + 4 * sub + ((lane & 15) >> 2);
       const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      voff[db][sub] = V_REGION + (64 * kh + key) * RB + ((((col >> 3) ^ swz<D>(key)) << 4) | ((col & 7) << 1));
+      voff[db][sub] = TILE_B + key * RB + ((((col >> 3) ^ swz<D>(key)) << 4) | ((col & 7) << 1));
     }
-
   typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
   const bf16x2v ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // one tile held in LDS buffer B
-  auto compute = [&](auto buf, int nvalid) {
-    constexpr int B = decltype(buf)::value;
-    if (64 * kh >= nvalid) return;  // this wave's key half is empty
-    const char* lds = smem + B * TILE_B;
-
-    // ---- S^T = K Q^T: 2 blocks of 32 keys x 32 queries
-    f32x16 s[2];
+  // one tile in LDS: S^T = K Q^T (4 blocks of 32 keys), softmax, O^T += V^T P^T
+  auto compute = [&](int nvalid) {
+    f32x16 s[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+    for (int kb = 0; kb < 4; ++kb) s[kb] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + koff[c] + 32 * kb * RB);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
-      }
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 a[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) a[kb] = *reinterpret_cast<const bf16x8*>(smem + koff[c] + 32 * kb * RB);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qf[c], s[kb], 0, 0, 0);
     }
-    // accumulator j of key block kb holds key 64*kh + 32*kb + 16*(j/8) + 8*half + j%8
+    // accumulator j of key block kb holds key 32*kb + 16*(j/8) + 8*half + j%8
     if (nvalid < kTile) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (64 * kh + 32 * kb + 16 * (j / 8) + 8 * half + (j % 8) >= nvalid) s[kb][j] = -INFINITY;
+          if (32 * kb + 16 * (j / 8) + 8 * half + (j % 8) >= nvalid) s[kb][j] = -INFINITY;
     }
-
-    // ---- online softmax (fp32), lazy rescaling; row sums of the bf16 probabilities
     float mx = s[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const bool need = (m_new - m_run) * c2 > 8.f;
+    const bool need = (m_new - m_run) * c2 > 8.f;  // lazy rescaling
     if (__ballot(need)) {
       const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c2) : 1.f;
       if (need) m_run = m_new;
@@ -327,10 +306,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
       for (int i = 0; i < ND; ++i) o[i] *= alpha;
     }
     const float mc = m_run * c2;
-    bf16x8 pb[4];  // P^T chunk t holds keys 64*kh + 16t + 8*half + e
+    bf16x8 pb[8];  // P^T chunk t holds keys 16t + 8*half + e
     float lsum = l_run;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         f32x8 pv;
@@ -344,68 +323,32 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
         lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 6, 7), ones, lsum, false);
       }
     l_run = lsum;
-
-    // ---- O^T += V^T P^T
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
+    for (int t = 0; t < 8; ++t) {
+      bf16x8 a[ND];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (UF_LDS i16x4*)(lds + voff[db][0] + 16 * t * RB));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (UF_LDS i16x4*)(lds + voff[db][1] + 16 * t * RB));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], o[db], 0, 0, 0);
+      for (int db = 0; db < ND; ++db) {
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((UF_LDS i16x4*)(smem + voff[db][0] + 16 * t * RB));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((UF_LDS i16x4*)(smem + voff[db][1] + 16 * t * RB));
+        a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
+#pragma unroll
+      for (int db = 0; db < ND; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], pb[t], o[db], 0, 0, 0);
     }
   };
 
-  // ---- main loop, unrolled by two so that the LDS buffer is a compile-time constant
-  int kt = next_tile();
-  if (kt >= 0) issue(kt, 0);
-  while (kt >= 0) {
-    const int kt1 = next_tile();
+  // ---- main loop: the other work-group on this CU computes while this one loads
+  for (int kt = next_tile(); kt >= 0; kt = next_tile()) {
+    issue(kt);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile kt is in buffer 0 for every wave; buffer 1 is free
-    if (kt1 >= 0) issue(kt1, 1);
-    compute(Buf<0>{}, min(kTile, p.n_k - kt * kTile));
-    if (kt1 < 0) break;
-    const int kt2 = next_tile();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile kt1 is in buffer 1; buffer 0 is free
-    if (kt2 >= 0) issue(kt2, 0);
-    compute(Buf<1>{}, min(kTile, p.n_k - kt1 * kTile));
-    kt = kt2;
+    __syncthreads();  // the tile is in LDS for every wave
+    compute(min(kTile, p.n_k - kt * kTile));
+    __syncthreads();  // every wave is done with the tile before the next one lands
   }
 
-  // ---- merge the two key halves of every row (LDS exchange), then write
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  __syncthreads();  // every wave is done with the tile buffers
-  float* xo = reinterpret_cast<float*>(smem);   // [rb][ND][16][64]
-  float* xm = xo + 4 * ND * 16 * 64;             // [rb][2][64]
-  if (kh == 1) {
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) xo[((rb * ND + db) * 16 + j) * 64 + lane] = o[db][j];
-    xm[(rb * 2 + 0) * 64 + lane] = m_run;
-    xm[(rb * 2 + 1) * 64 + lane] = l_tot;
-  }
-  __syncthreads();
-  if (kh == 1) return;
-
-  const float mb = xm[(rb * 2 + 0) * 64 + lane];
-  const float lb = xm[(rb * 2 + 1) * 64 + lane];
-  const float M = fmaxf(m_run, mb);
-  const float wa = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - M) * c2);
-  const float wb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mb - M) * c2);
-  const float l = l_tot * wa + lb * wb;
-#pragma unroll
-  for (int db = 0; db < ND; ++db)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) o[db][j] = o[db][j] * wa + xo[((rb * ND + db) * 16 + j) * 64 + lane] * wb;
+  // ---- epilogue.  O^T accumulator j of d block db holds d = 32*db + 8*(j/4) + 4*half + j%4.
+  const float l = l_run + __shfl_xor(l_run, 32);
   if (qi >= p.n_q) return;
-  // O^T accumulator j of d block db holds d = 32*db + 8*(j/4) + 4*half + j%4
   if (p.splits == 1) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)qi * p.o_stride_tok + (int64_t)head * p.o_stride_head;
@@ -427,7 +370,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnParams p) {
         *reinterpret_cast<f32x4*>(wo + 32 * db + 8 * g + 4 * half) = x;
       }
     if (half == 0) {
-      p.ws_ml[2 * row] = M * c2;  // -inf when this split saw no key
+      p.ws_ml[2 * row] = m_run * c2;  // -inf when this split saw no key
       p.ws_ml[2 * row + 1] = l;
     }
   }
