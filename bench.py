@@ -15,9 +15,10 @@ bounded sample of the same step on the host's cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -31,6 +32,25 @@ from synth import CONFIGS, TILE, bf16_bits_to_f32, draw_step_tensors, make_block
 METRIC = "attention TFLOP/s (% bf16 MFMA peak) + frames/s at 1K and 2K chunk shapes"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 FLOP/clk/CU)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_2k_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "windowed_attention_amd", "csrc", "uf_kernels.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    or None when that summary was taken on a different kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"sha256 `([0-9a-f]{64})`", text)
+    t = re.search(r"traffic_bytes_per_launch\[%s\]: (\d+)" % re.escape(workload), text)
+    if not m or not t or m.group(1) != src:
+        return None
+    return int(t.group(1))
 
 
 def log(msg):
@@ -277,6 +297,8 @@ def main():
         cpu = cpu_baseline(cfg, fill, args.cpu_budget)
 
     s = summary(main_r)
+    traffic_bytes = measured_traffic(cfg.name)
+    traffic_gbs = None if traffic_bytes is None else round(traffic_bytes / (main_r["attn_ms"] * 1e-3) / 1e9, 1)
     line = {
         "metric": METRIC,
         "value": round(main_r["tflops"], 3),
@@ -302,7 +324,9 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(main_r["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic_gbs,
+            "traffic_unit": "GB/s (rocprofv3 FETCH_SIZE + WRITE_SIZE bytes per launch / launch time)",
+            "traffic_bytes_per_launch": traffic_bytes,
             "launch_ms": round(main_r["attn_ms"], 4),
         },
         "cpu_baseline": cpu,
