@@ -319,7 +319,7 @@ def main():
         "append_gbs": round(main_r["append_gbs"], 1),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_kernel<128>",
+            "kernel": f"attn_kernel<{cfg.head_dim}>",
             "achieved": round(main_r["attn_tflops"], 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

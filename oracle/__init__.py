@@ -11,14 +11,19 @@ Contents
                 sliding-window mask.
   attention.py  softmax(Q K^T / sqrt(d)) V in float64 over a key set, with the
                 optional 128x128 block mask and grouped-query heads.
+  topk.py       the block mask a head chooses for itself: mean-pooled query and
+                key tiles, their dot-product scores, and the local window plus
+                the top-k best-scoring other key tiles of every row.
 
-Every function is pinned by tests in tests/test_oracle_pins.py (closed forms,
-invariants, the window tables derived from the pages, and PyTorch's
-scaled_dot_product_attention in float64 on small cases).  Parity unpinned:
+Every function is pinned by tests in tests/test_oracle_pins.py and
+tests/test_oracle_topk.py (closed forms, invariants, the window tables derived
+from the pages, a hand-worked top-k example, brute force over subsets, and
+PyTorch's scaled_dot_product_attention in float64 on small cases).  Parity unpinned:
 none.
 """
 from .window import FrameListWindow, sliding_window_allowed, visible_frames_after
 from .attention import attend, attend_full_sequence, executed_pairs
+from .topk import block_scores, local_tiles, pooled_tiles, topk_block_mask
 
 __all__ = [
     "FrameListWindow",
@@ -27,4 +32,8 @@ __all__ = [
     "attend",
     "attend_full_sequence",
     "executed_pairs",
+    "block_scores",
+    "local_tiles",
+    "pooled_tiles",
+    "topk_block_mask",
 ]

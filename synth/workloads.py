@@ -15,6 +15,14 @@ Shapes follow the latents the pages describe:
     patches give 90x156 tokens.
   * Streaming decoder: FlashDecoder review, model-components table (rolling
     cache of W_frm = 2 frames, G = 3 KV groups) with 12 query heads of 128.
+  * FlashDecoder-XL shapes: the model-scaling table's XL row (width 1536,
+    24 heads, 3 KV groups, so head_dim 64 and 8 query heads per KV head) on
+    720p latents, whose 16x spatial factor (model-components table, spatial
+    upsampling) gives a 45x80 token grid.  "decoder-xl" is the backbone's
+    per-frame window of W_frm = 2 frames; "refine-xl" is the temporal
+    refinement blocks, which take r_t = 4 frames per latent frame and keep a
+    window of r_t * W_frm = 8 frames (model-components table; Algorithm 1's
+    refinement cache update).
 """
 from __future__ import annotations
 
@@ -58,6 +66,8 @@ CONFIGS = [
     Workload(2, "decoder", "bf16", 12, 3, 128, (30, 52), 1, 2, 0, 120, None),
     Workload(3, "1k", "bf16", 12, 12, 128, (60, 104), 3, 6, 0, 4, 25),
     Workload(4, "2k", "bf16", 12, 12, 128, (90, 156), 3, 6, 0, 4, 15),
+    Workload(5, "decoder-xl", "bf16", 24, 3, 64, (45, 80), 1, 2, 0, 24, None),
+    Workload(6, "refine-xl", "bf16", 24, 3, 64, (45, 80), 4, 8, 0, 6, None),
 ]
 
 

@@ -4,8 +4,9 @@ Every test drives the HIP library through its C ABI (ctypes binding).  The
 oracle sees the same bf16 values widened to float64.  The bar is
 max-abs <= 2e-2 and relative L2 <= 5e-3 on every compared row.
 
-Full-size workloads (480P, decoder, 1K, 2K) stream all their steps in the
-library's default launch configuration; the oracle then checks whole query
+Full-size workloads (480P, decoder, 1K, 2K, FlashDecoder-XL backbone and
+refinement) stream all their steps in the library's default launch
+configuration; the oracle then checks whole query
 tiles of each checked step (first, last and seeded random tiles), which it
 computes row by row.  Reduced shapes are compared on every row.
 """
@@ -107,6 +108,16 @@ def test_1k_masked_stream():
 
 def test_2k_masked_stream():
     run_stream(CONFIGS[4], tiles=5)
+
+
+def test_decoder_xl_stream():
+    # head_dim 64, 24 query heads over 3 KV heads (8 per group), per-frame steps
+    run_stream(CONFIGS[5], check_steps=[0, 1, 2, 23], tiles=6)
+
+
+def test_refine_xl_stream():
+    # temporal refinement: 4-frame steps over an 8-frame window, head_dim 64, GQA 8
+    run_stream(CONFIGS[6], check_steps=[0, 1, 2, 5], tiles=5)
 
 
 # ---------------------------------------------------------------------------------------------
