@@ -186,6 +186,64 @@ def run_workload(cfg, warmup, steps):
     }
 
 
+def run_topk(cfg, steps, local_blocks=1):
+    """Block-mask generation (uf_block_mask_topk) at the workload's steady state, then attention
+    under the generated mask.  top_k = the workload's mask density times the key tiles, less the
+    local window (at least 0)."""
+    import torch
+    from windowed_attention_amd import KVCache, uf
+
+    F, L = cfg.frames_per_step, cfg.tokens_per_frame
+    fill = -(-(cfg.anchor_frames + cfg.window_frames) // F)
+    cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, cfg.window_frames, cfg.anchor_frames)
+    for s in range(fill + 1):
+        qb, kb, vb = draw_step_tensors(cfg, s)
+        cache.append(to_dev(kb), to_dev(vb), F)
+    q = to_dev(qb)
+    n_k = cache.window().n_keys
+    n_qb, n_kb = -(-cfg.q_tokens // TILE), -(-n_k // TILE)
+    pct = cfg.mask_pct or 100
+    top_k = max(0, (pct * n_kb + 50) // 100 - (2 + 2 * local_blocks))
+    mask = torch.empty((cfg.n_q_heads, n_qb, n_kb), dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty(uf.uf_block_mask_workspace_bytes(cache.desc, cfg.q_tokens, cfg.n_q_heads), dtype=torch.uint8,
+                     device="cuda:0")
+    out = torch.empty_like(q)
+    for _ in range(3):
+        cache.block_mask_topk(q, top_k, local_blocks, mask=mask, workspace=ws)
+        cache.attn_step(q, out, mask)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    gen_ms, attn_ms = [], []
+    for _ in range(steps):
+        ev[0].record()
+        cache.block_mask_topk(q, top_k, local_blocks, mask=mask, workspace=ws)
+        ev[1].record()
+        cache.attn_step(q, out, mask)
+        ev[2].record()
+        torch.cuda.synchronize()
+        gen_ms.append(ev[0].elapsed_time(ev[1]))
+        attn_ms.append(ev[1].elapsed_time(ev[2]))
+    cache.close()
+    m = mask.cpu().numpy()
+    flops = executed_flops(cfg.q_tokens, n_k, cfg.n_q_heads, cfg.head_dim, m)
+    # algorithmic bytes: q and the visible K read once, the mask written once
+    nbytes = 2 * cfg.head_dim * (cfg.q_tokens * cfg.n_q_heads + n_k * cfg.n_kv_heads) + m.size
+    g = float(np.mean(gen_ms))
+    a = float(np.mean(attn_ms))
+    return {
+        "top_k": top_k,
+        "local_blocks": local_blocks,
+        "kept_tiles_per_row": float(m.sum() / (m.shape[0] * m.shape[1])),
+        "mask_gen_ms": round(g, 4),
+        "mask_gen_gbs": round(nbytes / (g * 1e-3) / 1e9, 1),
+        "mask_gen_frac_hbm": round(nbytes / (g * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "mask_gen_bytes": nbytes,
+        "attn_ms": round(a, 4),
+        "attn_tflops": round(flops / (a * 1e-3) / 1e12, 2),
+        "pct_of_attn": round(100 * g / a, 2),
+    }
+
+
 def cpu_baseline(cfg, pool_step, budget_s=12.0):
     """The float64 oracle on a bounded sample of one steady step: whole query tiles, all heads."""
     import oracle
@@ -263,6 +321,7 @@ def main():
     ap.add_argument("--workload", default="2k", choices=[c.name for c in CONFIGS])
     ap.add_argument("--also", default="1k", help="comma-separated extra workloads reported under 'also' ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-topk", action="store_true", help="skip the block-mask generation leg")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work in the CPU baseline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 times), a known-size kernel "
@@ -291,6 +350,10 @@ def main():
         r = run_workload({c.name: c for c in CONFIGS}[name], args.warmup, args.steps)
         also[name] = summary(r)
         del r
+    topk = None
+    if not args.no_topk and cfg.mask_pct is not None:
+        log(f"{cfg.name}: top-k block-mask generation")
+        topk = run_topk(cfg, args.steps)
     cpu = None
     if not args.no_cpu_baseline:
         fill = -(-(cfg.anchor_frames + cfg.window_frames) // cfg.frames_per_step)
@@ -330,6 +393,7 @@ def main():
             "launch_ms": round(main_r["attn_ms"], 4),
         },
         "cpu_baseline": cpu,
+        "mask_topk": topk,
         "also": also,
     }
     print(json.dumps(line), flush=True)

@@ -213,6 +213,55 @@ uf_status uf_kvcache_window(const uf_kvcache* cache, uf_window_info* out);
 uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mask* block_mask,
                        uf_tensor* out, void* stream);
 
+/*
+ * Block-mask generation (Ultra Flash notes, key design 3, dynamic
+ * block-sparse causal attention): each head rates every (query tile, key
+ * tile) pair by the dot product of the two tiles' mean-pooled q and k, and
+ * keeps the best-rated key tiles beside a local window.
+ *
+ * top_k         key tiles kept by rating in every (head, query tile) row,
+ *               chosen among the tiles the local window does not already
+ *               keep; equal ratings go to the lower tile index; a row with
+ *               fewer candidates keeps them all.  >= 0.
+ * local_blocks  the local window: the key tiles overlapping the query tile's
+ *               own key positions (the step's queries are the newest Nq of
+ *               the n_keys keys, so query i sits at key n_keys - Nq + i),
+ *               widened by local_blocks tiles on each side.  >= 0.
+ */
+typedef struct uf_topk_params {
+  int32_t top_k;
+  int32_t local_blocks;
+} uf_topk_params;
+
+/* Workspace bytes uf_block_mask_topk needs for Nq = n_q_tokens queries of
+ * n_q_heads heads against any window of this cache description (fp32 tile
+ * means of q and of the largest window's keys); 0 if the request is invalid. */
+size_t uf_block_mask_workspace_bytes(const uf_kvcache_desc* desc, int32_t n_q_tokens, int32_t n_q_heads);
+
+/*
+ * Rate and select key tiles for a step's queries q ([Nq, Hq, head_dim] bf16,
+ * Hq a multiple of n_kv_heads, Nq <= the window's n_keys) against the keys
+ * the cache exposes now (call it after the step's append, before
+ * uf_attn_step).  Tiles are 128 tokens in query order and in key order; the
+ * last tile of each may be partial and is averaged over its own tokens.
+ *
+ * mask    device uint8 [Hq][ceil(Nq/128)][ceil(n_keys/128)], contiguous:
+ *         1 = keep, 0 = skip.  It is a valid uf_block_mask with n_heads = Hq,
+ *         stride_qblock = ceil(n_keys/128), stride_head = that times
+ *         ceil(Nq/128).
+ * scores  optional device float [same shape]: the ratings (plain dot
+ *         products of the fp32 tile means, no 1/sqrt(d)); NULL = not written.
+ * workspace  device memory of uf_block_mask_workspace_bytes bytes or more,
+ *         256-byte aligned, used only during the call's kernels.
+ * Means and ratings are fp32: each tile's rows summed in fp32, divided by
+ * the row count; ratings are fma chains over head_dim in order.  At most
+ * 3072 key tiles (UF_ERR_UNSUPPORTED beyond).  Nq == 0 is a no-op.  Two
+ * kernel launches on `stream`; the cache state does not change.
+ */
+uf_status uf_block_mask_topk(const uf_tensor* q, const uf_kvcache* cache, const uf_topk_params* params,
+                             uint8_t* mask, float* scores, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* Static string naming a status code. */
 const char* uf_status_string(uf_status status);
 

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     assert sorted(uf.EXPORTED) == names
     out = subprocess.run(["nm", "-D", "--defined-only", uf._LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (uf_\w+)$", out, flags=re.M))
@@ -207,5 +207,72 @@ def test_step_validation():
         # an empty query set is valid and launches nothing
         e = _tensor(0, 4, data=FAKE * 32)
         assert LIB.uf_attn_step(ctypes.byref(e), h, None, ctypes.byref(_tensor(0, 4, data=FAKE * 64)), None) == uf.UF_OK
+    finally:
+        uf.uf_kvcache_destroy(h)
+
+
+def test_block_mask_workspace_bytes():
+    d = desc(H=3, d=64, L=100, W=4, A=1)
+    # 250 queries of 6 heads: 2 tiles x 6 heads x 64 floats, rounded to 256 B; keys: ceil(500/128) = 4 tiles x 3 heads
+    assert uf.uf_block_mask_workspace_bytes(d, 250, 6) == 3072 + 4 * 3 * 64 * 4
+    assert uf.uf_block_mask_workspace_bytes(d, 250, 4) == 0      # 4 heads over 3 KV heads
+    assert uf.uf_block_mask_workspace_bytes(d, -1, 6) == 0
+    assert uf.uf_block_mask_workspace_bytes(desc(d=96), 10, 2) == 0
+
+
+def test_block_mask_topk_validation():
+    st, h = create(H=2, d=128, L=100, W=3, A=0)
+    assert st == uf.UF_OK
+    q = _tensor(200, 4, data=FAKE * 32)
+    p = uf.uf_topk_params(3, 1)
+    ws, ws_bytes = FAKE * 256, 1 << 20
+    mask = FAKE * 512
+
+    def call(qq=q, params=p, m=mask, sc=None, w=ws, wb=ws_bytes, handle=h):
+        pp = None if params is None else ctypes.byref(params)
+        return LIB.uf_block_mask_topk(ctypes.byref(qq), handle, pp, m, sc, w, wb, None)
+
+    try:
+        assert call() == uf.UF_ERR_STATE                                   # nothing appended
+        uf.uf_kvcache_append(h, None, None, 1, uf.UF_APPEND_COMMIT_ONLY, 0)  # 100 keys
+        assert call() == uf.UF_ERR_SHAPE                                   # 200 queries > 100 keys
+        uf.uf_kvcache_append(h, None, None, 2, uf.UF_APPEND_COMMIT_ONLY, 0)  # 300 keys
+        cases = [
+            (dict(handle=None), uf.UF_ERR_INVALID_ARG),
+            (dict(params=None), uf.UF_ERR_INVALID_ARG),
+            (dict(params=uf.uf_topk_params(-1, 0)), uf.UF_ERR_INVALID_ARG),
+            (dict(params=uf.uf_topk_params(2, -3)), uf.UF_ERR_INVALID_ARG),
+            (dict(qq=_tensor(200, 3, data=FAKE * 32)), uf.UF_ERR_SHAPE),     # 3 heads over 2 KV heads
+            (dict(qq=_tensor(200, 4, d=64, data=FAKE * 32)), uf.UF_ERR_SHAPE),
+            (dict(qq=_tensor(200, 4, data=FAKE * 32, dtype=2)), uf.UF_ERR_DTYPE),
+            (dict(m=None), uf.UF_ERR_INVALID_ARG),
+            (dict(w=None), uf.UF_ERR_INVALID_ARG),
+            (dict(wb=1024), uf.UF_ERR_INVALID_ARG),                           # workspace too small
+            (dict(w=ws + 64), uf.UF_ERR_INVALID_ARG),                         # misaligned workspace
+            (dict(m=ws + 4096), uf.UF_ERR_INVALID_ARG),                       # mask inside the workspace
+            (dict(sc=mask + 4), uf.UF_ERR_INVALID_ARG),                       # scores overlap the mask
+            (dict(sc=FAKE * 1024 + 2), uf.UF_ERR_INVALID_ARG),                # misaligned scores
+        ]
+        before = _window(h)
+        for kw, want in cases:
+            got = call(**kw)
+            assert got == want, (kw, uf.uf_status_string(got), uf.uf_last_error())
+            assert _window(h) == before
+        # no queries: valid, nothing launched
+        assert call(qq=_tensor(0, 4, data=FAKE * 32), m=None, w=None, wb=0) == uf.UF_OK
+    finally:
+        uf.uf_kvcache_destroy(h)
+
+
+def test_block_mask_topk_key_tile_limit():
+    # 3100 key tiles exceed what the selection kernel holds in LDS
+    st, h = create(H=1, d=64, L=128 * 3100, W=1, A=0)
+    assert st == uf.UF_OK
+    try:
+        uf.uf_kvcache_append(h, None, None, 1, uf.UF_APPEND_COMMIT_ONLY, 0)
+        q = _tensor(128, 1, d=64, data=FAKE * 32)
+        got = LIB.uf_block_mask_topk(ctypes.byref(q), h, ctypes.byref(uf.uf_topk_params(4, 0)), FAKE * 512, None,
+                                     FAKE * 256, 1 << 30, None)
+        assert got == uf.UF_ERR_UNSUPPORTED, uf.uf_last_error()
     finally:
         uf.uf_kvcache_destroy(h)

@@ -150,6 +150,13 @@ int device_cu_count() {
   return cached_cus;
 }
 
+// Bytes of the query-tile means in the mask-generation workspace, rounded up
+// so that the key-tile means after them start 256-byte aligned.
+size_t topk_workspace_split(int64_t q_tiles_times_heads, int head_dim) {
+  const size_t b = (size_t)q_tiles_times_heads * head_dim * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+
 }  // namespace
 
 extern "C" {
@@ -388,6 +395,76 @@ uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mas
     e = uf::launch_combine(c, d.head_dim, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
+  return UF_OK;
+}
+
+size_t uf_block_mask_workspace_bytes(const uf_kvcache_desc* desc, int32_t n_q_tokens, int32_t n_q_heads) {
+  if (!desc || check_desc(desc) != UF_OK || n_q_tokens < 0 || n_q_heads < 1 || n_q_heads % desc->n_kv_heads)
+    return 0;
+  const int64_t n_qb = ((int64_t)n_q_tokens + UF_TILE - 1) / UF_TILE;
+  const int64_t n_kb = (rows_per_head(*desc) + UF_TILE - 1) / UF_TILE;
+  return topk_workspace_split(n_qb * n_q_heads, desc->head_dim) +
+         (size_t)n_kb * desc->n_kv_heads * desc->head_dim * sizeof(float);
+}
+
+uf_status uf_block_mask_topk(const uf_tensor* q, const uf_kvcache* cache, const uf_topk_params* params,
+                             uint8_t* mask, float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cache) return fail(UF_ERR_INVALID_ARG, "cache is NULL");
+  if (!params) return fail(UF_ERR_INVALID_ARG, "params is NULL");
+  const auto& d = cache->d;
+  uf_status s;
+  if ((s = check_tensor(q, "q", d.head_dim)) != UF_OK) return s;
+  if (q->n_heads % d.n_kv_heads != 0)
+    return fail(UF_ERR_SHAPE, "query heads (%d) must be a multiple of KV heads (%d)", q->n_heads, d.n_kv_heads);
+  if (params->top_k < 0 || params->local_blocks < 0)
+    return fail(UF_ERR_INVALID_ARG, "top_k and local_blocks must be >= 0");
+  const uf_window_info w = window_of(d, cache->frames, cache->last_append, cache->active);
+  if (w.n_keys == 0) return fail(UF_ERR_STATE, "no frame appended yet");
+  const int32_t n_q = q->n_tokens, hq = q->n_heads;
+  if (n_q > w.n_keys)
+    return fail(UF_ERR_SHAPE, "%d queries but only %d visible keys: queries must be the newest keys", n_q, w.n_keys);
+  const int n_qb = (n_q + UF_TILE - 1) / UF_TILE;
+  const int n_kb = (w.n_keys + UF_TILE - 1) / UF_TILE;
+  if (n_kb > uf::kTopkMaxKeyTiles)
+    return fail(UF_ERR_UNSUPPORTED, "%d key tiles; mask generation handles at most %d", n_kb, uf::kTopkMaxKeyTiles);
+  if ((int64_t)n_qb * hq * n_kb >= kMaxIndex) return fail(UF_ERR_CAPACITY, "mask too large");
+  if (n_q == 0) return UF_OK;
+  if (!mask) return fail(UF_ERR_INVALID_ARG, "mask is NULL");
+  const size_t q_part = topk_workspace_split((int64_t)n_qb * hq, d.head_dim);
+  const size_t need = q_part + (size_t)n_kb * d.n_kv_heads * d.head_dim * sizeof(float);
+  if (!workspace || workspace_bytes < need)
+    return fail(UF_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : 0);
+  if ((uintptr_t)workspace & 255) return fail(UF_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t mask_bytes = (size_t)hq * n_qb * n_kb;
+  if (overlaps(mask, mask_bytes, workspace, need) || (scores && overlaps(scores, 4 * mask_bytes, workspace, need)) ||
+      (scores && overlaps(scores, 4 * mask_bytes, mask, mask_bytes)))
+    return fail(UF_ERR_INVALID_ARG, "mask, scores and workspace must not overlap");
+  if (((uintptr_t)scores & 3) != 0) return fail(UF_ERR_INVALID_ARG, "scores must be 4-byte aligned");
+
+  uf::TopkParams p;
+  p.q = (const uint16_t*)q->data;
+  p.q_stride_tok = q->stride_token;
+  p.q_stride_head = q->stride_head;
+  p.k = (const uint16_t*)d.k_storage;
+  p.kv_head_stride = rows_per_head(d) * d.head_dim;
+  p.n_q = n_q;
+  p.n_k = w.n_keys;
+  p.n_q_heads = hq;
+  p.n_kv_heads = d.n_kv_heads;
+  p.anchor_keys = w.anchor_keys;
+  p.ring_base = d.anchor_frames * d.tokens_per_frame;
+  p.ring_cap = w.ring_capacity_keys;
+  p.ring_rot = w.ring_rotation_keys;
+  p.n_qb = n_qb;
+  p.n_kb = n_kb;
+  p.top_k = std::min(params->top_k, n_kb);
+  p.local_blocks = std::min(params->local_blocks, n_kb);
+  p.qbar = (float*)workspace;
+  p.kbar = (float*)((char*)workspace + q_part);
+  p.mask = mask;
+  p.scores = scores;
+  hipError_t e = uf::launch_block_mask_topk(p, d.head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mask generation launch");
   return UF_OK;
 }
 

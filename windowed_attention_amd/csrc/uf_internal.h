@@ -65,8 +65,33 @@ struct CombineParams {
   int32_t n_q, n_q_heads, splits;
 };
 
+// Block-score top-k mask of one step: mean-pool the query tiles and the
+// visible key tiles, score every (head, query tile, key tile) triple, keep the
+// local window plus the top_k best other key tiles of each row.
+struct TopkParams {
+  const uint16_t* q;
+  int64_t q_stride_tok, q_stride_head;
+  const uint16_t* k;           // cache K storage base
+  int64_t kv_head_stride;      // rows_total * head_dim
+  int32_t n_q;                 // query rows (the newest n_q of the n_k keys)
+  int32_t n_k;                 // visible keys
+  int32_t n_q_heads, n_kv_heads;
+  int32_t anchor_keys, ring_base, ring_cap, ring_rot;  // key order -> storage row, as in AttnParams
+  int32_t n_qb, n_kb;          // query tiles, key tiles
+  int32_t top_k;               // scored tiles kept per row beyond the local window
+  int32_t local_blocks;        // tiles kept on each side of the diagonal tiles
+  float* qbar;                 // workspace [n_q_heads][n_qb][d] tile means of q
+  float* kbar;                 // workspace [n_kv_heads][d][n_kb] tile means of k, channel-major
+  uint8_t* mask;               // [n_q_heads][n_qb][n_kb]
+  float* scores;               // optional [n_q_heads][n_qb][n_kb]
+};
+
+// Key tiles per row that the selection kernel holds in LDS (4 rows per work-group).
+constexpr int kTopkMaxKeyTiles = 3072;
+
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_block_mask_topk(const TopkParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace uf

@@ -31,7 +31,8 @@ UF_MAX_APPEND_FRAMES = 64
 EXPORTED = [
     "uf_kvcache_storage_bytes", "uf_attn_workspace_bytes", "uf_kvcache_create", "uf_kvcache_destroy",
     "uf_kvcache_reset", "uf_kvcache_set_window", "uf_kvcache_append", "uf_kvcache_plan_append",
-    "uf_kvcache_window", "uf_attn_step", "uf_status_string", "uf_last_error",
+    "uf_kvcache_window", "uf_attn_step", "uf_block_mask_workspace_bytes", "uf_block_mask_topk",
+    "uf_status_string", "uf_last_error",
 ]
 
 
@@ -70,6 +71,10 @@ class uf_append_plan(ctypes.Structure):
                 ("window_after", uf_window_info)]
 
 
+class uf_topk_params(ctypes.Structure):
+    _fields_ = [("top_k", ctypes.c_int32), ("local_blocks", ctypes.c_int32)]
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built; run `python -m windowed_attention_amd.build`")
@@ -89,6 +94,9 @@ def _load():
         "uf_kvcache_window": (ctypes.c_int, [ctypes.c_void_p, P(uf_window_info)]),
         "uf_attn_step": (ctypes.c_int, [P(uf_tensor), ctypes.c_void_p, P(uf_block_mask), P(uf_tensor),
                                         ctypes.c_void_p]),
+        "uf_block_mask_workspace_bytes": (ctypes.c_size_t, [P(uf_kvcache_desc), ctypes.c_int32, ctypes.c_int32]),
+        "uf_block_mask_topk": (ctypes.c_int, [P(uf_tensor), ctypes.c_void_p, P(uf_topk_params), ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
         "uf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "uf_last_error": (ctypes.c_char_p, []),
     }
@@ -193,6 +201,26 @@ def uf_attn_step(q, handle: int, block_mask, out, stream=None) -> None:
                              _stream_handle(stream)), "uf_attn_step")
 
 
+def uf_block_mask_workspace_bytes(desc: uf_kvcache_desc, n_q_tokens: int, n_q_heads: int) -> int:
+    return _lib.uf_block_mask_workspace_bytes(ctypes.byref(desc), n_q_tokens, n_q_heads)
+
+
+def uf_block_mask_topk(q, handle: int, top_k: int, local_blocks: int, mask, scores, workspace,
+                       stream=None) -> None:
+    """mask: uint8 [Hq, q_tiles, k_tiles] contiguous; scores: float32 of that shape or None;
+    workspace: a device tensor of at least uf_block_mask_workspace_bytes bytes."""
+    import torch
+    if mask.dtype != torch.uint8 or not mask.is_contiguous():
+        raise ValueError("mask must be a contiguous uint8 tensor")
+    if scores is not None and (scores.dtype != torch.float32 or not scores.is_contiguous()):
+        raise ValueError("scores must be a contiguous float32 tensor")
+    params = uf_topk_params(top_k, local_blocks)
+    _check(_lib.uf_block_mask_topk(ctypes.byref(tensor_of(q)), handle, ctypes.byref(params), mask.data_ptr(),
+                                   None if scores is None else scores.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream_handle(stream)),
+           "uf_block_mask_topk")
+
+
 def uf_status_string(status: int) -> str:
     return _lib.uf_status_string(status).decode()
 
@@ -251,6 +279,23 @@ class KVCache:
     def attn_step(self, q, out, block_mask=None, stream=None):
         uf_attn_step(q, self.handle, block_mask, out, stream)
         return out
+
+    def block_mask_topk(self, q, top_k: int, local_blocks: int = 0, mask=None, scores=None, workspace=None,
+                        stream=None):
+        """Top-k block mask of q against the current window (uf_block_mask_topk).
+
+        mask / scores / workspace are allocated here when not given; returns mask."""
+        import torch
+        n_q, hq = q.shape[0], q.shape[1]
+        n_qb = -(-n_q // UF_TILE)
+        n_kb = -(-self.window().n_keys // UF_TILE)
+        if mask is None:
+            mask = torch.empty((hq, n_qb, n_kb), dtype=torch.uint8, device=q.device)
+        if workspace is None:
+            nbytes = uf_block_mask_workspace_bytes(self.desc, n_q, hq)
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        uf_block_mask_topk(q, self.handle, top_k, local_blocks, mask, scores, workspace, stream)
+        return mask
 
     def close(self):
         if self.handle:
