@@ -32,6 +32,21 @@ __device__ inline int xcd_contiguous(int b, int n) {
   return xcd * per + min(xcd, extra) + slot;
 }
 
+// Windowed order: work items are taken in windows of kXcds * kRun consecutive items, and
+// within a window each XCD gets kRun consecutive ones (kRun = the work-groups an XCD holds at
+// once: 32 CUs x 2).  All XCDs then work inside one window at a time, which keeps the
+// chip-wide working set (heads in flight) small for the last-level cache, while each XCD's
+// resident work-groups still hold neighbouring items for its L2.  The last, partial window
+// is split XCD-contiguously.
+constexpr int kRun = 64;
+__device__ inline int xcd_windowed(int b, int n) {
+  constexpr int W = kXcds * kRun;
+  const int full = (n / W) * W;
+  if (b >= full) return full + xcd_contiguous(b - full, n - full);
+  const int xcd = b % kXcds, slot = b / kXcds;
+  return (slot / kRun) * W + xcd * kRun + slot % kRun;
+}
+
 // ---------------------------------------------------------------------------
 // Append: token-major [t][h][c] -> head-major cache rows of the frame's slot.
 
@@ -136,7 +151,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
   const int rb = wave;  // row block
 
   // ---- work item
-  const int item = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int item = xcd_windowed(blockIdx.x, gridDim.x);
   const int qblk = item % p.n_qblk;
   const int rest = item / p.n_qblk;
   const int split = rest % p.splits;
