@@ -244,7 +244,7 @@ def run_topk(cfg, steps, local_blocks=1):
     }
 
 
-def cpu_baseline(cfg, pool_step, budget_s=12.0):
+def cpu_baseline(cfg, pool_step, budget_s=15.0):
     """The float64 oracle on a bounded sample of one steady step: whole query tiles, all heads."""
     import oracle
     from threadpoolctl import threadpool_info
@@ -273,10 +273,16 @@ def cpu_baseline(cfg, pool_step, budget_s=12.0):
         return dt, fl
 
     log(f"cpu baseline: oracle on {cfg.name} step {pool_step}")
-    t1, _ = timed([0])                                   # calibration: one query tile
-    n = int(max(1, min(n_qt - 1, budget_s / max(t1, 1e-3))))
-    tiles = list(range(1, 1 + n)) if n_qt > 1 else [0]
-    t_total, done_flops = timed(tiles)
+    timed([0])                                           # warm-up: first query tile, not counted
+    # whole query tiles, in order, until the budget is spent (or the step is done)
+    t_total, done_flops, tiles = 0.0, 0, []
+    for t in range(1 if n_qt > 1 else 0, n_qt):
+        dt, fl = timed([t])
+        t_total += dt
+        done_flops += fl
+        tiles.append(t)
+        if t_total >= budget_s:
+            break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     tflops = done_flops / t_total / 1e12
     step_flops = executed_flops(cfg.q_tokens, n_k, cfg.n_q_heads, cfg.head_dim, mask)
@@ -322,7 +328,7 @@ def main():
     ap.add_argument("--also", default="1k", help="comma-separated extra workloads reported under 'also' ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true", help="skip the block-mask generation leg")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work in the CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU baseline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 times), a known-size kernel "
                          "against which profiler byte counters are scaled")
