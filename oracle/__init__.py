@@ -14,10 +14,13 @@ Contents
   topk.py       the block mask a head chooses for itself: mean-pooled query and
                 key tiles, their dot-product scores, and the local window plus
                 the top-k best-scoring other key tiles of every row.
+  fp8.py        FP8 E4M3 encoding and static-scale quantization of q, k, v;
+                the FP8 path's attention is attend() on the dequantized values.
 
-Every function is pinned by tests in tests/test_oracle_pins.py and
-tests/test_oracle_topk.py (closed forms, invariants, the window tables derived
-from the pages, a hand-worked top-k example, brute force over subsets, and
+Every function is pinned by tests in tests/test_oracle_pins.py,
+tests/test_oracle_topk.py and tests/test_oracle_fp8.py (closed forms,
+invariants, the window tables derived from the pages, hand-worked top-k and
+E4M3 examples, brute force over subsets and over all E4M3 codes, and
 PyTorch's scaled_dot_product_attention in float64 on small cases).  Parity unpinned:
 none.
 """

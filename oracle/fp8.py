@@ -1,0 +1,73 @@
+"""FP8 (E4M3) encoding and static-scale quantization (oracle, test infrastructure).
+
+What is computed.  FlashDecoder review, inference optimisations: static,
+calibrated FP8 quantization for matrix products, with a quality cost the
+review reports (Table 2, the -Opt rows); the Ultra Flash README mirror's CLI
+table offers the same switch (--fp8, --fp8_sr) for its DiT models.  For the
+attention path this is read as:
+  * q, k and v are quantized to FP8 E4M3 with one static scale per tensor:
+    code = E4M3(x * (1 / scale)), the product taken in float32, the encoding
+    rounding to the nearest representable value (ties to the even code, a
+    value that rounds to zero keeping its sign) and saturating at +-448; the
+    value is then code * scale.
+  * The attention itself is the plain definition (oracle.attention.attend)
+    applied to those dequantized values in float64.
+
+E4M3 ("FP8 E4M3" of the OCP 8-bit floating point specification): 1 sign bit,
+4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 encodes
+subnormals m/8 * 2^-6; no infinities; S.1111.111 is NaN, so the largest
+finite magnitude is 1.75 * 2^8 = 448.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MAX_E4M3 = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """uint8 E4M3 codes -> float64 values (NaN for the two NaN codes)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((e == 15) & ((c & 7) == 7), np.nan, out)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float32 values -> uint8 E4M3 codes: nearest value, ties to the even code, saturating
+    at +-448 (finite inputs only)."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    if not np.isfinite(x).all():
+        raise ValueError("e4m3_encode takes finite values")
+    sign = np.signbit(x)
+    a = np.minimum(np.abs(x), MAX_E4M3)
+    # The representable magnitudes below 2^-6 are spaced 2^-9; in [2^e, 2^(e+1)) they are
+    # spaced 2^(e-3).  Round |x| / spacing to the nearest integer, ties to even.
+    _, fe = np.frexp(a)                      # a = f * 2^fe, f in [0.5, 1): binade e = fe - 1
+    e = np.clip(fe - 1, -6, 8).astype(np.float64)
+    spacing = np.exp2(e - 3)
+    n = np.rint(a / spacing)                 # numpy rounds halves to even; a / spacing is exact
+    value = n * spacing                      # n == 16 lands on 2^(e+1), the next binade's first value
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = value < 2.0 ** -6
+    code[sub] = np.rint(value[sub] / 2.0 ** -9).astype(np.int64)
+    nrm = ~sub
+    _, ve = np.frexp(value[nrm])
+    ev = (ve - 1).astype(np.int64)
+    mant = np.rint((value[nrm] / np.exp2(ev.astype(np.float64)) - 1.0) * 8.0).astype(np.int64)
+    code[nrm] = ((ev + 7) << 3) | mant
+    return (code | np.where(sign, 0x80, 0)).astype(np.uint8)
+
+
+def quantize(x: np.ndarray, scale: float) -> np.ndarray:
+    """Static-scale quantization: E4M3 codes of x * float32(1 / scale), the product in float32."""
+    inv = np.float32(1.0 / float(scale))
+    return e4m3_encode(np.asarray(x, dtype=np.float32) * inv)
+
+
+def dequantize(codes: np.ndarray, scale: float) -> np.ndarray:
+    """Values code * scale in float64."""
+    return e4m3_decode(codes) * float(scale)
