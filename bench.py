@@ -32,6 +32,7 @@ from synth import CONFIGS, TILE, bf16_bits_to_f32, draw_step_tensors, make_block
 METRIC = "attention TFLOP/s (% bf16 MFMA peak) + frames/s at 1K and 2K chunk shapes"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 FLOP/clk/CU)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense FP8 MFMA (twice the bf16 rate)
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_2k_traffic.md")
@@ -100,9 +101,12 @@ def attach_masks(cfg, pool, n_keys_per_step):
             item["mask"] = torch.from_numpy(m).to("cuda:0")
 
 
-def run_workload(cfg, warmup, steps):
+FP8_SCALES = (0.02, 0.015, 0.02)  # static q, k, v scales for N(0,1) draws (E4M3 range, no saturation)
+
+
+def run_workload(cfg, warmup, steps, fp8=False):
     import torch
-    from windowed_attention_amd import KVCache
+    from windowed_attention_amd import KVCache, uf
 
     F, L = cfg.frames_per_step, cfg.tokens_per_frame
     # the stream's first steps fill the window; later steps reuse the pool's steady-state inputs
@@ -111,7 +115,12 @@ def run_workload(cfg, warmup, steps):
     t0 = time.time()
     log(f"{cfg.name}: drawing {n_pool} steps of inputs")
     pool = prepare(cfg, n_pool)
-    cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, cfg.window_frames, cfg.anchor_frames)
+    if fp8:
+        q_s, k_s, v_s = FP8_SCALES
+        cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, cfg.window_frames, cfg.anchor_frames,
+                        kv_dtype=uf.UF_FP8_E4M3, q_scale=q_s, k_scale=k_s, v_scale=v_s)
+    else:
+        cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, cfg.window_frames, cfg.anchor_frames)
     # key counts per pool step follow the window bookkeeping of the library itself
     n_keys = []
     for s in range(n_pool):
@@ -167,7 +176,8 @@ def run_workload(cfg, warmup, steps):
     cache.close()
 
     total_flops = float(sum(flops))
-    append_bytes = 4 * F * L * cfg.n_kv_heads * cfg.head_dim * 2  # K and V, each read and written
+    # K and V, each read (bf16) and written (bf16, or one byte per element for FP8)
+    append_bytes = 2 * F * L * cfg.n_kv_heads * cfg.head_dim * (2 + (1 if fp8 else 2))
     ms_per_step = 1e3 * wall / steps
     return {
         "cfg": cfg,
@@ -328,6 +338,7 @@ def main():
     ap.add_argument("--also", default="1k", help="comma-separated extra workloads reported under 'also' ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true", help="skip the block-mask generation leg")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) cache leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU baseline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 times), a known-size kernel "
@@ -356,6 +367,15 @@ def main():
         r = run_workload({c.name: c for c in CONFIGS}[name], args.warmup, args.steps)
         also[name] = summary(r)
         del r
+    fp8 = None
+    if not args.no_fp8 and cfg.head_dim in (64, 128):
+        log(f"{cfg.name}: FP8 (E4M3) cache")
+        r8 = run_workload(cfg, args.warmup, args.steps, fp8=True)
+        fp8 = summary(r8)
+        fp8["scales_q_k_v"] = list(FP8_SCALES)
+        fp8["peak_fp8_tflops"] = PEAK_FP8_TFLOPS
+        fp8["pct_peak_fp8_attn_kernel"] = 100 * r8["attn_tflops"] / PEAK_FP8_TFLOPS
+        del r8
     topk = None
     if not args.no_topk and cfg.mask_pct is not None:
         log(f"{cfg.name}: top-k block-mask generation")
@@ -400,6 +420,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "mask_topk": topk,
+        "fp8": fp8,
         "also": also,
     }
     print(json.dumps(line), flush=True)

@@ -62,7 +62,10 @@ typedef enum uf_status {
   UF_ERR_UNSUPPORTED = -7   /* valid request this build does not implement (e.g. head_dim) */
 } uf_status;
 
-typedef enum uf_dtype { UF_BF16 = 0 } uf_dtype;
+typedef enum uf_dtype {
+  UF_BF16 = 0,     /* bfloat16 */
+  UF_FP8_E4M3 = 1  /* OCP FP8 E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits, max 448 */
+} uf_dtype;
 
 /* Flags of uf_kvcache_append. */
 #define UF_APPEND_OVERWRITE_NEWEST 1u /* rewrite the newest append's frames in place; counter unchanged */
@@ -95,12 +98,24 @@ typedef struct uf_tensor {
  * Cache description.  Storage for K and for V is caller-allocated device
  * memory of uf_kvcache_storage_bytes(desc) bytes each, laid out head-major
  * [n_kv_heads][(anchor_frames + window_frames) * tokens_per_frame][head_dim]
- * bf16 (FlashDecoder review, Eq. 4: K_t, V_t in R^{G x (W L) x D_h}).  Rows
+ * elements of kv_dtype (FlashDecoder review, Eq. 4: K_t, V_t in
+ * R^{G x (W L) x D_h}).  Rows
  * [0, A*L) hold the anchor frames in append order; rows [A*L, (A+W)*L) are
  * the ring, frame r (counting non-anchor frames from 0) in slot r mod W.
  * The workspace (optional, may be NULL with workspace_bytes 0) holds
  * split-KV partial results; uf_attn_workspace_bytes gives the size that
  * lets the library split whenever it wants to.  Must be 256-byte aligned.
+ *
+ * kv_dtype selects the storage element type.  UF_BF16 (0) stores the values
+ * appended.  UF_FP8_E4M3 stores one byte per element with static scales
+ * (FlashDecoder review, inference optimisations: statically calibrated FP8):
+ * k and v are stored as E4M3(x / k_scale) and E4M3(x / v_scale), and every
+ * step quantizes its queries as E4M3(q / q_scale); E4M3() rounds to nearest
+ * (ties to even; the quotient is x times the reciprocal of the float scale,
+ * computed in double and rounded to float, the product rounded to float) and
+ * saturates at +-448; a value that rounds to zero keeps its sign.  The step then attends over the dequantized
+ * values; its probabilities are rounded to E4M3 for the P.V product.  The
+ * scales are ignored for UF_BF16 and must be positive and finite for FP8.
  */
 typedef struct uf_kvcache_desc {
   int32_t n_kv_heads;       /* G >= 1 */
@@ -112,6 +127,10 @@ typedef struct uf_kvcache_desc {
   void* v_storage;
   void* workspace;
   size_t workspace_bytes;
+  int32_t kv_dtype;         /* uf_dtype of the storage: UF_BF16 (0) or UF_FP8_E4M3 */
+  float q_scale;            /* FP8 static scales (see above) */
+  float k_scale;
+  float v_scale;
 } uf_kvcache_desc;
 
 /*
@@ -242,7 +261,8 @@ size_t uf_block_mask_workspace_bytes(const uf_kvcache_desc* desc, int32_t n_q_to
  * Rate and select key tiles for a step's queries q ([Nq, Hq, head_dim] bf16,
  * Hq a multiple of n_kv_heads, Nq <= the window's n_keys) against the keys
  * the cache exposes now (call it after the step's append, before
- * uf_attn_step).  Tiles are 128 tokens in query order and in key order; the
+ * uf_attn_step); bf16 caches only (UF_ERR_UNSUPPORTED for an FP8 cache).
+ * Tiles are 128 tokens in query order and in key order; the
  * last tile of each may be partial and is averaged over its own tokens.
  *
  * mask    device uint8 [Hq][ceil(Nq/128)][ceil(n_keys/128)], contiguous:

@@ -6,7 +6,8 @@ review reports (Table 2, the -Opt rows); the Ultra Flash README mirror's CLI
 table offers the same switch (--fp8, --fp8_sr) for its DiT models.  For the
 attention path this is read as:
   * q, k and v are quantized to FP8 E4M3 with one static scale per tensor:
-    code = E4M3(x * (1 / scale)), the product taken in float32, the encoding
+    code = E4M3(x * (1 / scale)), the scale a float32, its reciprocal rounded to
+    float32 and the product taken in float32, the encoding
     rounding to the nearest representable value (ties to the even code, a
     value that rounds to zero keeping its sign) and saturating at +-448; the
     value is then code * scale.
@@ -63,11 +64,13 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
 
 
 def quantize(x: np.ndarray, scale: float) -> np.ndarray:
-    """Static-scale quantization: E4M3 codes of x * float32(1 / scale), the product in float32."""
-    inv = np.float32(1.0 / float(scale))
+    """Static-scale quantization: E4M3 codes of x * r, the product in float32, where the scale
+    is a float32 and r is its reciprocal rounded to float32."""
+    s = float(np.float32(scale))
+    inv = np.float32(1.0 / s)
     return e4m3_encode(np.asarray(x, dtype=np.float32) * inv)
 
 
 def dequantize(codes: np.ndarray, scale: float) -> np.ndarray:
-    """Values code * scale in float64."""
-    return e4m3_decode(codes) * float(scale)
+    """Values code * scale in float64, the scale taken as a float32."""
+    return e4m3_decode(codes) * float(np.float32(scale))

@@ -1,0 +1,170 @@
+"""FP8 (E4M3) cache on the GPU against the oracle.
+
+Storage: every appended value is quantized with the cache's static scale; the
+stored codes must equal the oracle's E4M3 codes, byte for byte, in the rows
+the ring model predicts.
+
+Attention: the oracle attends in float64 over the dequantized q, k and v (its
+plain definition).  The kernel differs from it by rounding the probabilities
+to E4M3 for the P.V product (and the row sums it divides by).  With weights p
+normalised to a maximum of 1, E4M3 rounding moves each weight by at most
+e_j = max(2^-4 p_j, 2^-10) (half an ulp: relative 2^-4 for normal codes,
+absolute 2^-10 below 2^-6; the kernel's running reference max can only be
+smaller than the true one, which only lowers the relative cut-off).  With the
+same rounded weights in numerator and denominator,
+    |out - ref| <= sum_j e_j |v_j - ref| / (sum_j p_j - sum_j e_j)
+               <= (sum_j e_j |v_j| + |ref| sum_j e_j) / (sum_j p_j - sum_j e_j),
+plus the bf16 rounding of the output (2^-9 |ref|).  The tests compute that
+bound per output element from the oracle's weights and require every element
+within it (and print how much of it was used).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.fp8 as f8
+from synth import TILE, Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
+from tests.gpu_util import errors, f32_of, to_dev
+from tests.ring_model import RingModel
+from windowed_attention_amd import KVCache, uf
+
+pytestmark = pytest.mark.gpu
+
+SCALES = (0.02, 0.015, 0.02)  # q, k, v: N(0,1) draws use E4M3's range without saturating
+
+
+def _fp8_cache(cfg, scales=SCALES):
+    q_s, k_s, v_s = scales
+    return KVCache(cfg.n_kv_heads, cfg.head_dim, cfg.tokens_per_frame, cfg.window_frames, cfg.anchor_frames,
+                   kv_dtype=uf.UF_FP8_E4M3, q_scale=q_s, k_scale=k_s, v_scale=v_s)
+
+
+@pytest.mark.parametrize("case", [(2, 128, 200, 4, 1, 2, 6), (3, 64, 96, 3, 0, 1, 7)],
+                         ids=lambda c: "H%d-d%d-L%d-W%d-A%d-F%d" % c[:6])
+def test_fp8_append_codes_bit_exact(case):
+    H, d, L, W, A, F, n = case
+    print(f"fp8 append case {case}", flush=True)
+    cfg = Workload(60, "f8-append", "bf16", H, H, d, (1, L), F, W, A, n, None)
+    cache = _fp8_cache(cfg)
+    cache.k_storage.zero_()
+    cache.v_storage.zero_()
+    model = RingModel(H, d, L, W, A)
+    for s in range(n):
+        _, kb, vb = draw_step_tensors(cfg, s, scale_q=1.0)
+        kb = kb.copy()
+        kb[0, 0, :4] = [0x4580, 0xC580, 0x3C00, 0x0000]  # +-4096 (saturate at +-448 * scale), 2^-7, 0
+        cache.append(to_dev(kb), to_dev(vb), F)
+        kc = f8.quantize(bf16_bits_to_f32(kb), SCALES[1]).astype(np.uint16)
+        vc = f8.quantize(bf16_bits_to_f32(vb), SCALES[2]).astype(np.uint16)
+        model.append(F, kc, vc)
+        torch.cuda.synchronize()
+        _same_codes(cache.k_storage, model.k, f"K codes, append {s}")
+        _same_codes(cache.v_storage, model.v, f"V codes, append {s}")
+    cache.close()
+
+
+def _same_codes(storage, want, what):
+    got = storage.cpu().numpy().astype(np.uint16)
+    bad = np.argwhere(got != want)
+    for h, r, c in bad[:8]:
+        g, w = int(got[h, r, c]), int(want[h, r, c])
+        print(f"  {what}: head {h} row {r} ch {c}: got 0x{g:02x} ({f8.e4m3_decode(np.array([g]))[0]}), "
+              f"want 0x{w:02x} ({f8.e4m3_decode(np.array([w]))[0]})", flush=True)
+    assert len(bad) == 0, f"{what}: {len(bad)} codes differ"
+
+
+def _bound(q, k, v, ref, mask, rows):
+    """Per-element bound of the E4M3 probability rounding (see the module docstring)."""
+    n_q_heads, d = q.shape[1], q.shape[2]
+    group = n_q_heads // k.shape[1]
+    out = np.zeros_like(ref)
+    row_tile = rows // TILE
+    for h in range(n_q_heads):
+        kh, vh = k[:, h // group, :], v[:, h // group, :]
+        for qt in np.unique(row_tile):
+            sel = np.nonzero(row_tile == qt)[0]
+            keys = np.ones(k.shape[0], dtype=bool)
+            if mask is not None:
+                keys = np.repeat(mask[0 if mask.shape[0] == 1 else h, qt] != 0, TILE)[:k.shape[0]]
+            if not keys.any():
+                continue
+            s = q[rows[sel], h, :] @ kh[keys].T / math.sqrt(d)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            e = np.maximum(2.0 ** -4 * p, 2.0 ** -10)
+            # sum_j e_j |v_j - ref| <= sum_j e_j |v_j| + |ref| sum_j e_j
+            num = e @ np.abs(vh[keys]) + np.abs(ref[sel, h, :]) * e.sum(axis=1)[:, None]
+            out[sel, h, :] = num / (p.sum(axis=1) - e.sum(axis=1))[:, None]
+    return out + 2.0 ** -9 * np.abs(ref) + 1e-6
+
+
+def run_fp8_stream(cfg, check_steps=None, tiles=None, scales=SCALES):
+    q_s, k_s, v_s = scales
+    cache = _fp8_cache(cfg, scales)
+    win = oracle.FrameListWindow(cfg.tokens_per_frame, cfg.window_frames, cfg.anchor_frames)
+    check_steps = range(cfg.steps) if check_steps is None else check_steps
+    worst = 0.0
+    for s in range(cfg.steps):
+        qb, kb, vb = draw_step_tensors(cfg, s)
+        q_d = to_dev(qb)
+        print(f"{cfg.name} step {s}: fp8 append + attend", flush=True)
+        cache.append(to_dev(kb), to_dev(vb), cfg.frames_per_step)
+        win.append(f8.dequantize(f8.quantize(bf16_bits_to_f32(kb), k_s), k_s),
+                   f8.dequantize(f8.quantize(bf16_bits_to_f32(vb), v_s), v_s), cfg.frames_per_step)
+        n_k = cache.window().n_keys
+        mask_np = mask_d = None
+        if cfg.mask_pct is not None:
+            mask_np = make_block_mask(cfg.index, s, cfg.n_q_heads, cfg.q_tokens, n_k, cfg.mask_pct)
+            mask_d = torch.from_numpy(mask_np).to("cuda:0")
+        out = torch.empty_like(q_d)
+        cache.attn_step(q_d, out, mask_d)
+        if s not in check_steps:
+            continue
+        torch.cuda.synchronize()
+        got = f32_of(out)
+        nqt = -(-cfg.q_tokens // TILE)
+        sel_tiles = range(nqt) if tiles is None else sorted({0, nqt - 1, *range(1, nqt - 1, max(1, nqt // tiles))})
+        rows = np.concatenate([np.arange(t * TILE, min((t + 1) * TILE, cfg.q_tokens)) for t in sel_tiles])
+        qq = f8.dequantize(f8.quantize(bf16_bits_to_f32(qb), q_s), q_s)
+        kk, vv = win.keys_values()
+        ref = oracle.attend(qq, kk, vv, mask_np, rows=rows)
+        bound = _bound(qq, kk, vv, ref, mask_np, rows)
+        err = np.abs(got[rows].astype(np.float64) - ref)
+        ratio = float((err / bound).max())
+        ma, rl = errors(got[rows], ref)
+        print(f"  {cfg.name} step {s}: max_abs={ma:.3e} rel_l2={rl:.3e}, largest error / bound = {ratio:.3f}",
+              flush=True)
+        assert np.isfinite(got[rows]).all()
+        assert ratio <= 1.0, f"{cfg.name} step {s}: error beyond the E4M3 probability bound ({ratio:.3f})"
+        worst = max(worst, ratio)
+    cache.close()
+    return worst
+
+
+FP8_CASES = [
+    Workload(61, "f8-anchor", "bf16", 4, 2, 128, (10, 20), 3, 6, 3, 6, None),    # anchor + ring, GQA 2
+    Workload(62, "f8-mask", "bf16", 4, 4, 128, (12, 17), 2, 4, 0, 5, 40),         # per-head mask, ragged
+    Workload(63, "f8-d64", "bf16", 8, 2, 64, (9, 31), 2, 4, 1, 4, None),          # head_dim 64, GQA 4
+]
+
+
+@pytest.mark.parametrize("cfg", FP8_CASES, ids=lambda c: c.name)
+def test_fp8_attention_within_bound(cfg):
+    run_fp8_stream(cfg)
+
+
+def test_fp8_forced_splits(monkeypatch):
+    monkeypatch.setenv("UF_SPLITS", "3")
+    run_fp8_stream(Workload(64, "f8-split", "bf16", 4, 1, 128, (10, 30), 2, 4, 1, 4, None))
+
+
+def test_fp8_1k_shape():
+    cfg = Workload(3, "1k", "bf16", 12, 12, 128, (60, 104), 3, 6, 0, 2, 25)
+    run_fp8_stream(cfg, check_steps=[0, 1], tiles=4)
+
+
+def test_fp8_other_scales():
+    # a coarser q scale and a finer v scale
+    run_fp8_stream(Workload(65, "f8-scales", "bf16", 2, 2, 128, (8, 25), 1, 3, 0, 4, None), scales=(0.05, 0.01, 0.005))

@@ -276,3 +276,47 @@ def test_block_mask_topk_key_tile_limit():
         assert got == uf.UF_ERR_UNSUPPORTED, uf.uf_last_error()
     finally:
         uf.uf_kvcache_destroy(h)
+
+
+def fp8_desc(scales=(0.05, 0.02, 0.03), dtype=uf.UF_FP8_E4M3, **kw):
+    d = desc(**kw)
+    d.kv_dtype = dtype
+    d.q_scale, d.k_scale, d.v_scale = scales
+    return d
+
+
+def test_fp8_cache_description():
+    assert uf.uf_kvcache_storage_bytes(fp8_desc(H=3, d=64, L=100, W=4, A=1)) == 3 * 500 * 64
+    assert uf.uf_kvcache_storage_bytes(desc(H=3, d=64, L=100, W=4, A=1)) == 3 * 500 * 64 * 2
+    bad = [
+        (fp8_desc(dtype=5), uf.UF_ERR_DTYPE),
+        (fp8_desc(scales=(0.0, 1.0, 1.0)), uf.UF_ERR_INVALID_ARG),
+        (fp8_desc(scales=(1.0, -1.0, 1.0)), uf.UF_ERR_INVALID_ARG),
+        (fp8_desc(scales=(1.0, 1.0, float("inf"))), uf.UF_ERR_INVALID_ARG),
+        (fp8_desc(scales=(1.0, 1.0, float("nan"))), uf.UF_ERR_INVALID_ARG),
+        (fp8_desc(scales=(1e-45, 1.0, 1.0)), uf.UF_ERR_INVALID_ARG),   # reciprocal overflows float
+    ]
+    for d, want in bad:
+        h = ctypes.c_void_p()
+        got = LIB.uf_kvcache_create(ctypes.byref(d), ctypes.byref(h))
+        assert got == want, (uf.uf_status_string(got), uf.uf_last_error())
+        assert uf.uf_kvcache_storage_bytes(d) == 0
+    # scales are ignored for bf16 caches
+    d = fp8_desc(dtype=uf.UF_BF16, scales=(0.0, 0.0, 0.0))
+    h = ctypes.c_void_p()
+    assert LIB.uf_kvcache_create(ctypes.byref(d), ctypes.byref(h)) == uf.UF_OK
+    uf.uf_kvcache_destroy(h.value)
+
+
+def test_mask_generation_rejects_fp8_cache():
+    d = fp8_desc(H=2, d=128, L=100, W=3)
+    h = ctypes.c_void_p()
+    assert LIB.uf_kvcache_create(ctypes.byref(d), ctypes.byref(h)) == uf.UF_OK
+    try:
+        uf.uf_kvcache_append(h.value, None, None, 2, uf.UF_APPEND_COMMIT_ONLY, 0)
+        q = _tensor(100, 4, data=FAKE * 32)
+        got = LIB.uf_block_mask_topk(ctypes.byref(q), h.value, ctypes.byref(uf.uf_topk_params(2, 0)), FAKE * 512,
+                                     None, FAKE * 256, 1 << 20, None)
+        assert got == uf.UF_ERR_UNSUPPORTED, uf.uf_last_error()
+    finally:
+        uf.uf_kvcache_destroy(h.value)

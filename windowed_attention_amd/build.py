@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libuf.so")
 ARCH = "gfx950"
 
-SOURCES = ["uf_api.cpp", "uf_kernels.hip", "uf_topk.hip"]
+SOURCES = ["uf_api.cpp", "uf_kernels.hip", "uf_topk.hip", "uf_attn_fp8.hip"]
 
 # Packed fp32 VALU ops stay disabled on every device pass (-packed-fp32-ops).
 FLAGS = [

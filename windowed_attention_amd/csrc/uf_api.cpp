@@ -55,8 +55,19 @@ uf_status check_desc(const uf_kvcache_desc* d) {
   const int64_t rows = (int64_t)(d->anchor_frames + (int64_t)d->window_frames) * d->tokens_per_frame;
   if (rows >= kMaxIndex || rows * d->head_dim >= kMaxIndex * 64)
     return fail(UF_ERR_CAPACITY, "cache of %lld rows per head is too large", (long long)rows);
+  if (d->kv_dtype != UF_BF16 && d->kv_dtype != UF_FP8_E4M3)
+    return fail(UF_ERR_DTYPE, "kv_dtype must be UF_BF16 or UF_FP8_E4M3 (got %d)", d->kv_dtype);
+  if (d->kv_dtype == UF_FP8_E4M3) {
+    const float sc[3] = {d->q_scale, d->k_scale, d->v_scale};
+    for (float x : sc)
+      if (!(x > 0.f) || !isfinite(x) || !isfinite(1.0f / x))
+        return fail(UF_ERR_INVALID_ARG, "FP8 scales must be positive, finite and invertible");
+  }
   return UF_OK;
 }
+
+int elem_bytes(const uf_kvcache_desc& d) { return d.kv_dtype == UF_FP8_E4M3 ? 1 : 2; }
+float inv_scale(float s) { return (float)(1.0 / (double)s); }
 
 int64_t rows_per_head(const uf_kvcache_desc& d) {
   return ((int64_t)d.anchor_frames + d.window_frames) * d.tokens_per_frame;
@@ -163,7 +174,7 @@ extern "C" {
 
 size_t uf_kvcache_storage_bytes(const uf_kvcache_desc* desc) {
   if (!desc || check_desc(desc) != UF_OK) return 0;
-  return (size_t)desc->n_kv_heads * rows_per_head(*desc) * desc->head_dim * 2;
+  return (size_t)desc->n_kv_heads * rows_per_head(*desc) * desc->head_dim * elem_bytes(*desc);
 }
 
 size_t uf_attn_workspace_bytes(const uf_kvcache_desc* desc) {
@@ -275,7 +286,16 @@ uf_status uf_kvcache_append(uf_kvcache* cache, const uf_tensor* k_new, const uf_
     p.anchor_frames = d.anchor_frames;
     p.window_frames = d.window_frames;
     p.first_frame = overwrite ? cache->frames - n_frames : cache->frames;
-    hipError_t e = uf::launch_append(p, (hipStream_t)stream);
+    hipError_t e;
+    if (d.kv_dtype == UF_FP8_E4M3) {
+      uf::AppendFp8Params f;
+      f.a = p;
+      f.inv_scale[0] = inv_scale(d.k_scale);
+      f.inv_scale[1] = inv_scale(d.v_scale);
+      e = uf::launch_append_fp8(f, (hipStream_t)stream);
+    } else {
+      e = uf::launch_append(p, (hipStream_t)stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "append launch");
   }
   if (!overwrite) {
@@ -380,7 +400,17 @@ uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mas
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d.head_dim));
   p.ws_o = (float*)d.workspace;
   p.ws_ml = splits > 1 ? (float*)d.workspace + (size_t)splits * rows * d.head_dim : nullptr;
-  hipError_t e = uf::launch_attention(p, d.head_dim, (hipStream_t)stream);
+  hipError_t e;
+  if (d.kv_dtype == UF_FP8_E4M3) {
+    uf::AttnFp8Params f;
+    f.a = p;
+    f.a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d.head_dim) * (double)d.q_scale * (double)d.k_scale);
+    f.q_inv_scale = inv_scale(d.q_scale);
+    f.v_scale = d.v_scale;
+    e = uf::launch_attention_fp8(f, d.head_dim, (hipStream_t)stream);
+  } else {
+    e = uf::launch_attention(p, d.head_dim, (hipStream_t)stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (splits > 1) {
     uf::CombineParams c;
@@ -412,6 +442,7 @@ uf_status uf_block_mask_topk(const uf_tensor* q, const uf_kvcache* cache, const 
   if (!cache) return fail(UF_ERR_INVALID_ARG, "cache is NULL");
   if (!params) return fail(UF_ERR_INVALID_ARG, "params is NULL");
   const auto& d = cache->d;
+  if (d.kv_dtype != UF_BF16) return fail(UF_ERR_UNSUPPORTED, "mask generation reads bf16 caches only");
   uf_status s;
   if ((s = check_tensor(q, "q", d.head_dim)) != UF_OK) return s;
   if (q->n_heads % d.n_kv_heads != 0)

@@ -57,6 +57,19 @@ struct AttnParams {
   float* ws_ml;                // [splits][n_q][n_q_heads][2]: running max (log2 units), sum
 };
 
+// FP8 (E4M3) cache: the same append with each value quantized, code = E4M3(x * inv_scale),
+// saturating at +-448; and the attention step on the FP8 storage.
+struct AppendFp8Params {
+  AppendParams a;              // dst[] point to uint8 storage; head_dim counts elements (bytes)
+  float inv_scale[2];          // 1 / k_scale, 1 / v_scale
+};
+
+struct AttnFp8Params {
+  AttnParams a;                // k, v point to uint8 storage; scale_log2 = log2(e) q_scale k_scale / sqrt(d)
+  float q_inv_scale;           // q is quantized as E4M3(q * q_inv_scale)
+  float v_scale;               // O = v_scale * sum_j P_j V8_j / sum_j P_j
+};
+
 struct CombineParams {
   const float* ws_o;
   const float* ws_ml;
@@ -93,5 +106,7 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_block_mask_topk(const TopkParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_append_fp8(const AppendFp8Params& p, hipStream_t stream);
+hipError_t launch_attention_fp8(const AttnFp8Params& p, int head_dim, hipStream_t stream);
 
 }  // namespace uf

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "uf_device.h"
 #include "uf_internal.h"
 
 namespace uf {
@@ -21,32 +22,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;   // 4 waves of 64
 constexpr int kTile = 128;      // keys per tile = block-mask tile
-constexpr int kXcds = 8;        // MI355X: 8 XCDs, work-groups dealt round-robin
-
-// Work-group b is dispatched to XCD b % 8.  Renumber so that each XCD gets
-// one contiguous run of work items (neighbouring query blocks of the same
-// head), which then share K/V tiles in that XCD's L2.
-__device__ inline int xcd_contiguous(int b, int n) {
-  const int per = n / kXcds, extra = n % kXcds;
-  const int xcd = b % kXcds, slot = b / kXcds;
-  return xcd * per + min(xcd, extra) + slot;
-}
-
-// Windowed order: work items are taken in windows of kXcds * kRun consecutive items, and
-// within a window each XCD gets kRun consecutive ones (kRun = the work-groups an XCD holds at
-// once: 32 CUs x 2).  All XCDs then work inside one window at a time, which keeps the
-// chip-wide working set (heads in flight) small for the last-level cache, while each XCD's
-// resident work-groups still hold neighbouring items for its L2.  The last, partial window
-// is split XCD-contiguously.
-constexpr int kRun = 64;
-__device__ inline int xcd_windowed(int b, int n) {
-  constexpr int W = kXcds * kRun;
-  const int full = (n / W) * W;
-  if (b >= full) return full + xcd_contiguous(b - full, n - full);
-  const int xcd = b % kXcds, slot = b / kXcds;
-  return (slot / kRun) * W + xcd * kRun + slot % kRun;
-}
-
 // ---------------------------------------------------------------------------
 // Append: token-major [t][h][c] -> head-major cache rows of the frame's slot.
 
@@ -106,16 +81,6 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendParams p) {
 // 16-byte chunks of every row permuted by an XOR swizzle (swz below).
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-#define UF_LDS __attribute__((address_space(3)))
-#define UF_GLOBAL __attribute__((address_space(1)))
-
-__device__ inline int rowperm(int m) {  // swap bits 2 and 3 (an involution)
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
-__device__ inline void load_lds16(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds((const UF_GLOBAL void*)src, (UF_LDS void*)lds_dst, 16, 0, 0);
-}
 
 // Chunk swizzle of LDS row r: its 16-byte chunk c is stored at position
 // c ^ swz(r).  Chosen (exhaustively over linear maps of r mod 16) so that

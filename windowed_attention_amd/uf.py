@@ -23,6 +23,7 @@ UF_ERR_STATE = -5
 UF_ERR_HIP = -6
 UF_ERR_UNSUPPORTED = -7
 UF_BF16 = 0
+UF_FP8_E4M3 = 1
 UF_APPEND_OVERWRITE_NEWEST = 1
 UF_APPEND_COMMIT_ONLY = 2
 UF_TILE = 128
@@ -47,7 +48,8 @@ class uf_kvcache_desc(ctypes.Structure):
                 ("tokens_per_frame", ctypes.c_int32), ("window_frames", ctypes.c_int32),
                 ("anchor_frames", ctypes.c_int32), ("k_storage", ctypes.c_void_p),
                 ("v_storage", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("kv_dtype", ctypes.c_int32),
+                ("q_scale", ctypes.c_float), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class uf_block_mask(ctypes.Structure):
@@ -242,15 +244,17 @@ class KVCache:
     """
 
     def __init__(self, n_kv_heads: int, head_dim: int, tokens_per_frame: int, window_frames: int,
-                 anchor_frames: int = 0, device="cuda", workspace: bool = True):
+                 anchor_frames: int = 0, device="cuda", workspace: bool = True, kv_dtype: int = UF_BF16,
+                 q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0):
         import torch
         desc = uf_kvcache_desc(n_kv_heads, head_dim, tokens_per_frame, window_frames, anchor_frames,
-                               None, None, None, 0)
+                               None, None, None, 0, kv_dtype, q_scale, k_scale, v_scale)
         nbytes = uf_kvcache_storage_bytes(desc)
         if nbytes == 0:
             _check(_lib.uf_kvcache_create(ctypes.byref(desc), ctypes.byref(ctypes.c_void_p())), "KVCache")
         rows = (anchor_frames + window_frames) * tokens_per_frame
-        self.k_storage = torch.empty((n_kv_heads, rows, head_dim), dtype=torch.bfloat16, device=device)
+        tdt = torch.uint8 if kv_dtype == UF_FP8_E4M3 else torch.bfloat16
+        self.k_storage = torch.empty((n_kv_heads, rows, head_dim), dtype=tdt, device=device)
         self.v_storage = torch.empty_like(self.k_storage)
         ws_bytes = uf_attn_workspace_bytes(desc) if workspace else 0
         self.workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
