@@ -16,9 +16,11 @@ Contents
                 the top-k best-scoring other key tiles of every row.
   fp8.py        FP8 E4M3 encoding and static-scale quantization of q, k, v;
                 the FP8 path's attention is attend() on the dequantized values.
+  blocks.py     the (2, 8, 8) spatio-temporal block order of a step's tokens.
 
 Every function is pinned by tests in tests/test_oracle_pins.py,
-tests/test_oracle_topk.py and tests/test_oracle_fp8.py (closed forms,
+tests/test_oracle_topk.py, tests/test_oracle_fp8.py and
+tests/test_oracle_blocks.py (closed forms,
 invariants, the window tables derived from the pages, hand-worked top-k and
 E4M3 examples, brute force over subsets and over all E4M3 codes, and
 PyTorch's scaled_dot_product_attention in float64 on small cases).  Parity unpinned:
