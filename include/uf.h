@@ -116,6 +116,20 @@ typedef struct uf_tensor {
  * saturates at +-448; a value that rounds to zero keeps its sign.  The step then attends over the dequantized
  * values; its probabilities are rounded to E4M3 for the P.V product.  The
  * scales are ignored for UF_BF16 and must be positive and finite for FP8.
+ *
+ * Block order (Ultra Flash notes, key design 3: the block-sparse mask is over
+ * (2,8,8) spatio-temporal blocks).  With block_grid_h/w set, every append of
+ * F frames (F the same for the whole stream, dividing anchor_frames and
+ * window_frames) stores the step's tokens, given in raster order (frame, row,
+ * column), in block order: the frame pairs' full (2,8,8) blocks, pair by pair,
+ * blocks row-major, inside a block frame, row, column; then the odd last
+ * frame's full 8x8 patches; then every remaining token (rows from
+ * 8*floor(H/8) on, or columns from 8*floor(W/8) on) in raster order.  Key
+ * order and 128-token key tiles follow that order.  A step's queries must be
+ * the step's F*L tokens, given and returned in raster order; query row i
+ * (the unit of query tiles and mask rows) is the token at block position i.
+ * The attention output does not depend on the order: it only changes which
+ * tokens share a tile.
  */
 typedef struct uf_kvcache_desc {
   int32_t n_kv_heads;       /* G >= 1 */
@@ -131,6 +145,8 @@ typedef struct uf_kvcache_desc {
   float q_scale;            /* FP8 static scales (see above) */
   float k_scale;
   float v_scale;
+  int32_t block_grid_h;     /* 0, or the frame's token grid (block_grid_h * block_grid_w = L): */
+  int32_t block_grid_w;     /* each step is held in (2,8,8) block order (see below) */
 } uf_kvcache_desc;
 
 /*

@@ -320,3 +320,30 @@ def test_mask_generation_rejects_fp8_cache():
         assert got == uf.UF_ERR_UNSUPPORTED, uf.uf_last_error()
     finally:
         uf.uf_kvcache_destroy(h.value)
+
+
+def test_block_order_validation():
+    def mk(**kw):
+        d = desc(**kw)
+        return d
+    d = mk(H=2, d=128, L=200, W=4, A=2)
+    d.block_grid_h, d.block_grid_w = 10, 21       # 210 != 200 tokens
+    h = ctypes.c_void_p()
+    assert LIB.uf_kvcache_create(ctypes.byref(d), ctypes.byref(h)) == uf.UF_ERR_SHAPE
+    d.block_grid_h, d.block_grid_w = 10, 0
+    assert LIB.uf_kvcache_create(ctypes.byref(d), ctypes.byref(h)) == uf.UF_ERR_SHAPE
+    d.block_grid_h, d.block_grid_w = 10, 20
+    assert LIB.uf_kvcache_create(ctypes.byref(d), ctypes.byref(h)) == uf.UF_OK
+    try:
+        # 3 frames do not divide 2 anchor / 4 window frames
+        assert LIB.uf_kvcache_append(h, None, None, 3, uf.UF_APPEND_COMMIT_ONLY, None) == uf.UF_ERR_SHAPE
+        assert LIB.uf_kvcache_append(h, None, None, 2, uf.UF_APPEND_COMMIT_ONLY, None) == uf.UF_OK
+        # the stream's steps keep their frame count
+        assert LIB.uf_kvcache_append(h, None, None, 1, uf.UF_APPEND_COMMIT_ONLY, None) == uf.UF_ERR_STATE
+        assert LIB.uf_kvcache_append(h, None, None, 2, uf.UF_APPEND_COMMIT_ONLY, None) == uf.UF_OK
+        q, out = _tensor(300, 4, data=FAKE * 32), _tensor(300, 4, data=FAKE * 64)
+        assert LIB.uf_attn_step(ctypes.byref(q), h, None, ctypes.byref(out), None) == uf.UF_ERR_SHAPE  # not 400
+        uf.uf_kvcache_reset(h)
+        assert LIB.uf_kvcache_append(h, None, None, 1, uf.UF_APPEND_COMMIT_ONLY, None) == uf.UF_OK  # new stream
+    finally:
+        uf.uf_kvcache_destroy(h)

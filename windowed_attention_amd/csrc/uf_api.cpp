@@ -18,6 +18,7 @@ struct uf_kvcache {
   int64_t frames;       // frames appended since create / reset
   int32_t last_append;  // frames in the newest append
   int32_t active;       // recent frames visible (crop), 1..W
+  int32_t block_frames; // block order: frames per step of this stream (0 until the first append)
 };
 
 namespace {
@@ -55,6 +56,10 @@ uf_status check_desc(const uf_kvcache_desc* d) {
   const int64_t rows = (int64_t)(d->anchor_frames + (int64_t)d->window_frames) * d->tokens_per_frame;
   if (rows >= kMaxIndex || rows * d->head_dim >= kMaxIndex * 64)
     return fail(UF_ERR_CAPACITY, "cache of %lld rows per head is too large", (long long)rows);
+  if ((d->block_grid_h == 0) != (d->block_grid_w == 0) || d->block_grid_h < 0 || d->block_grid_w < 0 ||
+      (d->block_grid_h && (int64_t)d->block_grid_h * d->block_grid_w != d->tokens_per_frame))
+    return fail(UF_ERR_SHAPE, "block grid %d x %d does not give %d tokens per frame", d->block_grid_h,
+                d->block_grid_w, d->tokens_per_frame);
   if (d->kv_dtype != UF_BF16 && d->kv_dtype != UF_FP8_E4M3)
     return fail(UF_ERR_DTYPE, "kv_dtype must be UF_BF16 or UF_FP8_E4M3 (got %d)", d->kv_dtype);
   if (d->kv_dtype == UF_FP8_E4M3) {
@@ -111,6 +116,14 @@ uf_status check_append_request(const uf_kvcache* c, int32_t n_frames, uint32_t f
       return fail(UF_ERR_STATE, "overwrite must cover the newest append exactly (%d frames, got %d)",
                   c->last_append, n_frames);
     return UF_OK;
+  }
+  if (d.block_grid_h && n_frames > 0) {
+    if (c->block_frames && n_frames != c->block_frames)
+      return fail(UF_ERR_STATE, "block order: every append of the stream has %d frames (got %d)", c->block_frames,
+                  n_frames);
+    if (d.anchor_frames % n_frames || d.window_frames % n_frames)
+      return fail(UF_ERR_SHAPE, "block order: %d frames per append must divide anchor (%d) and window (%d) frames",
+                  n_frames, d.anchor_frames, d.window_frames);
   }
   const int64_t first = c->frames;
   const int64_t anchor_left = std::max<int64_t>(0, d.anchor_frames - first);
@@ -201,6 +214,7 @@ uf_status uf_kvcache_create(const uf_kvcache_desc* desc, uf_kvcache** out) {
   c->frames = 0;
   c->last_append = 0;
   c->active = desc->window_frames;
+  c->block_frames = 0;
   *out = c;
   return UF_OK;
 }
@@ -215,6 +229,7 @@ uf_status uf_kvcache_reset(uf_kvcache* cache) {
   cache->frames = 0;
   cache->last_append = 0;
   cache->active = cache->d.window_frames;
+  cache->block_frames = 0;
   return UF_OK;
 }
 
@@ -286,6 +301,8 @@ uf_status uf_kvcache_append(uf_kvcache* cache, const uf_tensor* k_new, const uf_
     p.anchor_frames = d.anchor_frames;
     p.window_frames = d.window_frames;
     p.first_frame = overwrite ? cache->frames - n_frames : cache->frames;
+    p.blk_h = d.block_grid_h;
+    p.blk_w = d.block_grid_w;
     hipError_t e;
     if (d.kv_dtype == UF_FP8_E4M3) {
       uf::AppendFp8Params f;
@@ -302,6 +319,7 @@ uf_status uf_kvcache_append(uf_kvcache* cache, const uf_tensor* k_new, const uf_
     cache->frames += n_frames;
     cache->last_append = n_frames;
   }
+  if (d.block_grid_h) cache->block_frames = n_frames;
   return UF_OK;
 }
 
@@ -325,6 +343,9 @@ uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mas
   if (overlaps(out->data, out_bytes, q->data, tensor_extent_bytes(*q)) ||
       overlaps(out->data, out_bytes, d.k_storage, kv_bytes) || overlaps(out->data, out_bytes, d.v_storage, kv_bytes))
     return fail(UF_ERR_INVALID_ARG, "out overlaps q or the cache");
+  if (d.block_grid_h && n_q != 0 && (int64_t)n_q != (int64_t)cache->block_frames * d.tokens_per_frame)
+    return fail(UF_ERR_SHAPE, "block order: the queries must be the step's %lld tokens (got %d)",
+                (long long)cache->block_frames * d.tokens_per_frame, n_q);
   const int n_qt = (n_q + UF_TILE - 1) / UF_TILE;
   const int n_kt = (w.n_keys + UF_TILE - 1) / UF_TILE;
   if (mask) {
@@ -400,6 +421,9 @@ uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mas
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d.head_dim));
   p.ws_o = (float*)d.workspace;
   p.ws_ml = splits > 1 ? (float*)d.workspace + (size_t)splits * rows * d.head_dim : nullptr;
+  p.blk_h = d.block_grid_h;
+  p.blk_w = d.block_grid_w;
+  p.blk_frames = cache->block_frames;
   hipError_t e;
   if (d.kv_dtype == UF_FP8_E4M3) {
     uf::AttnFp8Params f;
@@ -454,6 +478,9 @@ uf_status uf_block_mask_topk(const uf_tensor* q, const uf_kvcache* cache, const 
   const int32_t n_q = q->n_tokens, hq = q->n_heads;
   if (n_q > w.n_keys)
     return fail(UF_ERR_SHAPE, "%d queries but only %d visible keys: queries must be the newest keys", n_q, w.n_keys);
+  if (d.block_grid_h && n_q != 0 && (int64_t)n_q != (int64_t)cache->block_frames * d.tokens_per_frame)
+    return fail(UF_ERR_SHAPE, "block order: the queries must be the step's %lld tokens (got %d)",
+                (long long)cache->block_frames * d.tokens_per_frame, n_q);
   const int n_qb = (n_q + UF_TILE - 1) / UF_TILE;
   const int n_kb = (w.n_keys + UF_TILE - 1) / UF_TILE;
   if (n_kb > uf::kTopkMaxKeyTiles)
@@ -494,6 +521,9 @@ uf_status uf_block_mask_topk(const uf_tensor* q, const uf_kvcache* cache, const 
   p.kbar = (float*)((char*)workspace + q_part);
   p.mask = mask;
   p.scores = scores;
+  p.blk_h = d.block_grid_h;
+  p.blk_w = d.block_grid_w;
+  p.blk_frames = cache->block_frames;
   hipError_t e = uf::launch_block_mask_topk(p, d.head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "mask generation launch");
   return UF_OK;

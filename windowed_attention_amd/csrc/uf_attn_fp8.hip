@@ -81,7 +81,8 @@ __global__ void __launch_bounds__(kThreads) append_fp8_kernel(AppendFp8Params p)
     const int64_t gf = a.first_frame + f;
     const int64_t slot = gf < a.anchor_frames ? gf : a.anchor_frames + (gf - a.anchor_frames) % a.window_frames;
     const int64_t row = slot * a.tokens_per_frame + tf;
-    const uint16_t* sp = src + t * a.src_stride_tok[which] + h * a.src_stride_head[which] + c * 16;
+    const uint32_t ts = a.blk_h ? (uint32_t)block_src_token((int)t, a.n_tok / a.tokens_per_frame, a.blk_h, a.blk_w) : t;
+    const uint16_t* sp = src + ts * a.src_stride_tok[which] + h * a.src_stride_head[which] + c * 16;
     const uint4 v0 = *reinterpret_cast<const uint4*>(sp);
     const uint4 v1 = *reinterpret_cast<const uint4*>(sp + 8);
     uint4 out;
@@ -135,12 +136,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
   const int q_tile = q0 / kTile;
   const int head = hgrp * p.heads_per_wg + rb / waves_per_head;
   const int qi = q0 + (rb % waves_per_head) * 32 + l32;
+  const int qt = p.blk_h && qi < p.n_q ? block_src_token(qi, p.blk_frames, p.blk_h, p.blk_w) : qi;
 
   // ---- Q^T fragments (B operand): lane (query, half) holds channels 64c + 32 half .. +31
   i32x8 qf[NCH];
   {
     const bool ok = qi < p.n_q;
-    const uint16_t* qp = p.q + (int64_t)(ok ? qi : 0) * p.q_stride_tok + (int64_t)head * p.q_stride_head + 32 * half;
+    const uint16_t* qp = p.q + (int64_t)(ok ? qt : 0) * p.q_stride_tok + (int64_t)head * p.q_stride_head + 32 * half;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       i32x8 x;
@@ -345,7 +347,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
   if (qi >= p.n_q) return;
   if (p.splits == 1) {
     const float inv = l > 0.f ? pp.v_scale / l : 0.f;
-    __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)qi * p.o_stride_tok + (int64_t)head * p.o_stride_head;
+    __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)qt * p.o_stride_tok + (int64_t)head * p.o_stride_head;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -354,7 +356,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g + 4 * half) = __builtin_convertvector(x, bf16x4);
       }
   } else {
-    const int64_t row = ((int64_t)split * p.n_q + qi) * p.n_q_heads + head;
+    const int64_t row = ((int64_t)split * p.n_q + qt) * p.n_q_heads + head;
     float* wo = p.ws_o + row * D;
 #pragma unroll
     for (int db = 0; db < ND; ++db)

@@ -46,4 +46,41 @@ __device__ inline void load_lds16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds((const UF_GLOBAL void*)src, (UF_LDS void*)lds_dst, 16, 0, 0);
 }
 
+// Raster token (frame f, row y, column x -> (f H + y) W + x) at position i of a step's
+// block order, for F frames of an H x W grid (Ultra Flash notes, key design 3: (2,8,8)
+// spatio-temporal blocks): first the frame pairs' full (2,8,8) blocks (pair by pair, blocks
+// row-major, inside a block frame, row, column), then the odd last frame's full 8x8 patches,
+// then every token outside a full block or patch in raster order.
+__device__ inline int block_src_token(int i, int F, int H, int W) {
+  const int hb = H >> 3, wb = W >> 3, nb = hb * wb;
+  const int region_a = (F >> 1) * nb * 128;
+  if (i < region_a) {
+    const int p = i / (nb * 128), rem = i - p * nb * 128;
+    const int b = rem >> 7, w = rem & 127;
+    const int y = 8 * (b / wb) + ((w >> 3) & 7), x = 8 * (b % wb) + (w & 7);
+    return ((2 * p + (w >> 6)) * H + y) * W + x;
+  }
+  i -= region_a;
+  const int region_b = (F & 1) * nb * 64;
+  if (i < region_b) {
+    const int b = i >> 6, w = i & 63;
+    return ((F - 1) * H + 8 * (b / wb) + (w >> 3)) * W + 8 * (b % wb) + (w & 7);
+  }
+  i -= region_b;
+  const int edge = H * W - 64 * nb;           // tokens of a frame outside full blocks
+  const int f = i / edge, k = i - f * edge;
+  const int right = W - 8 * wb;               // columns right of the last full block
+  const int beside = 8 * hb * right;          // leftover tokens in the block rows
+  int y, x;
+  if (k < beside) {
+    y = k / right;
+    x = 8 * wb + (k - y * right);
+  } else {
+    const int k2 = k - beside;
+    y = 8 * hb + k2 / W;
+    x = k2 - (k2 / W) * W;
+  }
+  return (f * H + y) * W + x;
+}
+
 }  // namespace uf

@@ -24,6 +24,7 @@ struct AppendParams {
   int32_t anchor_frames;       // A
   int32_t window_frames;       // W
   int64_t first_frame;         // global index of the first appended frame
+  int32_t blk_h, blk_w;        // != 0: destination token t takes source token block_src_token(t)
 };
 
 // One attention step.  The grid is a flat list of work items
@@ -55,6 +56,7 @@ struct AttnParams {
   float scale_log2;            // log2(e) / sqrt(d)
   float* ws_o;                 // [splits][n_q][n_q_heads][d] unnormalised partial outputs
   float* ws_ml;                // [splits][n_q][n_q_heads][2]: running max (log2 units), sum
+  int32_t blk_h, blk_w, blk_frames;  // != 0: query row i is token block_src_token(i) of q and out
 };
 
 // FP8 (E4M3) cache: the same append with each value quantized, code = E4M3(x * inv_scale),
@@ -97,6 +99,7 @@ struct TopkParams {
   float* kbar;                 // workspace [n_kv_heads][d][n_kb] tile means of k, channel-major
   uint8_t* mask;               // [n_q_heads][n_qb][n_kb]
   float* scores;               // optional [n_q_heads][n_qb][n_kb]
+  int32_t blk_h, blk_w, blk_frames;  // != 0: query row i is token block_src_token(i) of q
 };
 
 // Key tiles per row that the selection kernel holds in LDS (4 rows per work-group).

@@ -42,7 +42,9 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendParams p) {
     const int64_t gf = p.first_frame + f;
     const int64_t slot = gf < p.anchor_frames ? gf : p.anchor_frames + (gf - p.anchor_frames) % p.window_frames;
     const int64_t row = slot * p.tokens_per_frame + tf;
-    const uint4 val = *reinterpret_cast<const uint4*>(src + t * p.src_stride_tok[which] +
+    // block order: the step's frames sit in consecutive slots and row t takes source token pi(t)
+    const uint32_t ts = p.blk_h ? (uint32_t)block_src_token((int)t, p.n_tok / p.tokens_per_frame, p.blk_h, p.blk_w) : t;
+    const uint4 val = *reinterpret_cast<const uint4*>(src + ts * p.src_stride_tok[which] +
                                                       h * p.src_stride_head[which] + c * 8);
     *reinterpret_cast<uint4*>(dst + ((int64_t)h * p.rows_total + row) * p.head_dim + c * 8) = val;
   }
@@ -127,12 +129,14 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
   const int q_tile = q0 / kTile;  // block-mask row
   const int head = hgrp * p.heads_per_wg + rb / waves_per_head;
   const int qi = q0 + (rb % waves_per_head) * 32 + l32;  // this lane's query row
+  // its token in q and out (differs from qi when the step is held in block order)
+  const int qt = p.blk_h && qi < p.n_q ? block_src_token(qi, p.blk_frames, p.blk_h, p.blk_w) : qi;
 
   // ---- Q^T fragments (B operand), in registers for the whole key range
   bf16x8 qf[NC];
   {
     const bool ok = qi < p.n_q;
-    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(ok ? qi : 0) * p.q_stride_tok +
+    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(ok ? qt : 0) * p.q_stride_tok +
                        (int64_t)head * p.q_stride_head + 8 * half;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -331,7 +335,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
   if (qi >= p.n_q) return;
   if (p.splits == 1) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)qi * p.o_stride_tok + (int64_t)head * p.o_stride_head;
+    __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)qt * p.o_stride_tok + (int64_t)head * p.o_stride_head;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -340,7 +344,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g + 4 * half) = __builtin_convertvector(x, bf16x4);
       }
   } else {
-    const int64_t row = ((int64_t)split * p.n_q + qi) * p.n_q_heads + head;
+    const int64_t row = ((int64_t)split * p.n_q + qt) * p.n_q_heads + head;
     float* wo = p.ws_o + row * D;
 #pragma unroll
     for (int db = 0; db < ND; ++db)

@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "uf_device.h"
 #include "uf_internal.h"
 
 namespace uf {
@@ -66,7 +67,8 @@ __global__ void __launch_bounds__(kThreads) pool_kernel(TopkParams p) {
 #pragma unroll 4
   for (int r = r0; r < n_rows; r += RP) {
     const int tok = tile * kTile + r;
-    const uint16_t* src = is_q ? p.q + (int64_t)tok * p.q_stride_tok + (int64_t)head * p.q_stride_head
+    const int qtok = p.blk_h ? block_src_token(tok, p.blk_frames, p.blk_h, p.blk_w) : tok;
+    const uint16_t* src = is_q ? p.q + (int64_t)qtok * p.q_stride_tok + (int64_t)head * p.q_stride_head
                                : p.k + (int64_t)head * p.kv_head_stride + key_row(p, tok) * D;
     const uint4 v = *reinterpret_cast<const uint4*>(src + c * 8);
     acc[0] += bf16_lo(v.x);

@@ -49,7 +49,8 @@ class uf_kvcache_desc(ctypes.Structure):
                 ("anchor_frames", ctypes.c_int32), ("k_storage", ctypes.c_void_p),
                 ("v_storage", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("kv_dtype", ctypes.c_int32),
-                ("q_scale", ctypes.c_float), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+                ("q_scale", ctypes.c_float), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("block_grid_h", ctypes.c_int32), ("block_grid_w", ctypes.c_int32)]
 
 
 class uf_block_mask(ctypes.Structure):
@@ -245,10 +246,11 @@ class KVCache:
 
     def __init__(self, n_kv_heads: int, head_dim: int, tokens_per_frame: int, window_frames: int,
                  anchor_frames: int = 0, device="cuda", workspace: bool = True, kv_dtype: int = UF_BF16,
-                 q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0):
+                 q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0, block_grid=(0, 0)):
         import torch
         desc = uf_kvcache_desc(n_kv_heads, head_dim, tokens_per_frame, window_frames, anchor_frames,
-                               None, None, None, 0, kv_dtype, q_scale, k_scale, v_scale)
+                               None, None, None, 0, kv_dtype, q_scale, k_scale, v_scale,
+                               block_grid[0], block_grid[1])
         nbytes = uf_kvcache_storage_bytes(desc)
         if nbytes == 0:
             _check(_lib.uf_kvcache_create(ctypes.byref(desc), ctypes.byref(ctypes.c_void_p())), "KVCache")
