@@ -104,7 +104,7 @@ def attach_masks(cfg, pool, n_keys_per_step):
 FP8_SCALES = (0.02, 0.015, 0.02)  # static q, k, v scales for N(0,1) draws (E4M3 range, no saturation)
 
 
-def run_workload(cfg, warmup, steps, fp8=False):
+def run_workload(cfg, warmup, steps, fp8=False, block_order=False):
     import torch
     from windowed_attention_amd import KVCache, uf
 
@@ -115,12 +115,13 @@ def run_workload(cfg, warmup, steps, fp8=False):
     t0 = time.time()
     log(f"{cfg.name}: drawing {n_pool} steps of inputs")
     pool = prepare(cfg, n_pool)
+    kw = {"block_grid": cfg.grid} if block_order else {}
     if fp8:
         q_s, k_s, v_s = FP8_SCALES
         cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, cfg.window_frames, cfg.anchor_frames,
-                        kv_dtype=uf.UF_FP8_E4M3, q_scale=q_s, k_scale=k_s, v_scale=v_s)
+                        kv_dtype=uf.UF_FP8_E4M3, q_scale=q_s, k_scale=k_s, v_scale=v_s, **kw)
     else:
-        cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, cfg.window_frames, cfg.anchor_frames)
+        cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, cfg.window_frames, cfg.anchor_frames, **kw)
     # key counts per pool step follow the window bookkeeping of the library itself
     n_keys = []
     for s in range(n_pool):
@@ -339,6 +340,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true", help="skip the block-mask generation leg")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) cache leg")
+    ap.add_argument("--no-block-order", action="store_true", help="skip the (2,8,8) block-order leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU baseline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 times), a known-size kernel "
@@ -376,6 +378,12 @@ def main():
         fp8["peak_fp8_tflops"] = PEAK_FP8_TFLOPS
         fp8["pct_peak_fp8_attn_kernel"] = 100 * r8["attn_tflops"] / PEAK_FP8_TFLOPS
         del r8
+    blk = None
+    if not args.no_block_order:
+        log(f"{cfg.name}: (2,8,8) block order")
+        rb = run_workload(cfg, args.warmup, args.steps, block_order=True)
+        blk = summary(rb)
+        del rb
     topk = None
     if not args.no_topk and cfg.mask_pct is not None:
         log(f"{cfg.name}: top-k block-mask generation")
@@ -421,6 +429,7 @@ def main():
         "cpu_baseline": cpu,
         "mask_topk": topk,
         "fp8": fp8,
+        "block_order": blk,
         "also": also,
     }
     print(json.dumps(line), flush=True)
