@@ -285,15 +285,16 @@ def cpu_baseline(cfg, pool_step, budget_s=15.0):
 
     log(f"cpu baseline: oracle on {cfg.name} step {pool_step}")
     timed([0])                                           # warm-up: first query tile, not counted
-    # whole query tiles, in order, until the budget is spent (or the step is done)
+    # whole query tiles, in order and 8 to a call, until the budget is spent (or the step is done)
     t_total, done_flops, tiles = 0.0, 0, []
-    for t in range(1 if n_qt > 1 else 0, n_qt):
-        dt, fl = timed([t])
+    t = 1 if n_qt > 1 else 0
+    while t < n_qt and t_total < budget_s:
+        chunk = list(range(t, min(t + 8, n_qt)))
+        dt, fl = timed(chunk)
         t_total += dt
         done_flops += fl
-        tiles.append(t)
-        if t_total >= budget_s:
-            break
+        tiles += chunk
+        t = chunk[-1] + 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     tflops = done_flops / t_total / 1e12
     step_flops = executed_flops(cfg.q_tokens, n_k, cfg.n_q_heads, cfg.head_dim, mask)
