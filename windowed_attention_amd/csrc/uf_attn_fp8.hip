@@ -94,7 +94,20 @@ __global__ void __launch_bounds__(kThreads) append_fp8_kernel(AppendFp8Params p)
 
 // ---------------------------------------------------------------------------
 // Attention.  Work-group and schedule as in the bf16 kernel: 4 waves, 128 (query, head)
-// rows, one wave per 32-query row block, two work-groups per CU, one K and one V tile in LDS.
+// rows, one wave per 32-query row block, two work-groups per CU.  FP8 tiles are half the
+// bytes of bf16 ones, so each work-group double-buffers its K and V tiles in the same LDS
+// the bf16 kernel single-buffers in: the copy of the next kept tile runs under the
+// computation of the current one.
+
+// Global -> LDS copy of 16 bytes per lane (lane i's bytes land at lds_dst + 16 i), as inline
+// asm: the instruction has no register result, and written this way the compiler does not
+// take it for an LDS store that every later LDS read must wait for, which would hold the
+// reads of the current tile until the next tile's copy has landed.  The callers wait for
+// the copies themselves (s_waitcnt vmcnt(0) before the barrier that publishes a tile).
+__device__ inline void copy16_async(const void* src, void* lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(UF_LDS void*)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+}
 
 // 16-byte chunk swizzle of LDS row r (rows of D bytes): chunk c sits at c ^ swz(r), which
 // spreads both the 16-lane row-strided K reads and the 8-row transpose reads of V over
@@ -117,7 +130,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
   constexpr int RPI = 64 / CPR;           // rows written by one wave-wide 16-byte load
   constexpr int NW = kThreads / 64;
   constexpr int NLD = kTile / RPI / NW;   // such loads per wave, per tensor and tile
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_B];  // [K tile][V tile]
+  constexpr int BUF_B = 2 * TILE_B;       // one buffer: [K tile][V tile]
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -205,10 +219,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
     const int row = (wave * NLD + i) * RPI + lane / CPR;
     lane_off[i] = row * RB + (((lane % CPR) ^ swz8<D>(row)) << 4);
   }
-  auto issue = [&](int kt) {
+  auto issue = [&](int kt, int buf) {
     const int j0 = kt * kTile;
     const int nvalid = min(kTile, p.n_k - j0);
-    char* kd = smem + wave * NLD * 1024;
+    char* kd = smem + buf * BUF_B + wave * NLD * 1024;
     char* vd = kd + TILE_B;
     int r0 = -1;
     if (nvalid == kTile) {
@@ -225,8 +239,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
       const uint8_t* vt_base = vbase + (int64_t)r0 * RB;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        load_lds16(kt_base + lane_off[i], kd + i * 1024);
-        load_lds16(vt_base + lane_off[i], vd + i * 1024);
+        copy16_async(kt_base + lane_off[i], kd + i * 1024);
+        copy16_async(vt_base + lane_off[i], vd + i * 1024);
       }
     } else {
 #pragma unroll
@@ -234,8 +248,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
         const int row = (wave * NLD + i) * RPI + lane / CPR;
         const int chunk = (lane % CPR) ^ swz8<D>(row);
         const int64_t off = (int64_t)key_row(j0 + min(row, nvalid - 1)) * RB + chunk * 16;
-        load_lds16(kbase + off, kd + i * 1024);
-        load_lds16(vbase + off, vd + i * 1024);
+        copy16_async(kbase + off, kd + i * 1024);
+        copy16_async(vbase + off, vd + i * 1024);
       }
     }
   };
@@ -266,7 +280,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
   };
 
-  auto compute = [&](int nvalid) {
+  auto compute = [&](int nvalid, int buf) {
+    const char* tb = smem + buf * BUF_B;
     f32x16 s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) s[kb] = f32x16{};
@@ -274,8 +289,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
     for (int c = 0; c < NCH; ++c) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(smem + koff[c][0] + 32 * kb * RB);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(smem + koff[c][1] + 32 * kb * RB);
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(tb + koff[c][0] + 32 * kb * RB);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(tb + koff[c][1] + 32 * kb * RB);
         const i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         s[kb] = mfma8(a, qf[c], s[kb]);
       }
@@ -325,7 +340,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (UF_LDS i32x2*)(smem + voff[db] + (64 * t + 16 * r) * RB));
+              (UF_LDS i32x2*)(tb + voff[db] + (64 * t + 16 * r) * RB));
           a[2 * r] = v[0];
           a[2 * r + 1] = v[1];
         }
@@ -334,12 +349,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
     }
   };
 
-  for (int kt = next_tile(); kt >= 0; kt = next_tile()) {
-    issue(kt);
+  // Tile i sits in buffer i % 2.  The barrier at the top of step i publishes tile i (every
+  // wave has waited for its own copies) and also shows that every wave has finished tile
+  // i - 1, whose buffer the copy of tile i + 1 then overwrites.
+  int kt = next_tile();
+  int buf = 0;
+  if (kt >= 0) issue(kt, 0);
+  while (kt >= 0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    compute(min(kTile, p.n_k - kt * kTile));
-    __syncthreads();
+    const int kn = next_tile();
+    if (kn >= 0) issue(kn, buf ^ 1);
+    compute(min(kTile, p.n_k - kt * kTile), buf);
+    kt = kn;
+    buf ^= 1;
   }
 
   // ---- epilogue.  O^T accumulator j of d block db holds d = 32*db + 8*(j/4) + 4*half + j%4.
