@@ -108,6 +108,15 @@ __device__ inline void copy16_async(const void* src, void* lds_dst) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(UF_LDS void*)lds_dst);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
 }
+// The same from a wave-uniform base plus a 32-bit per-lane byte offset (the scalar-base
+// form of the instruction: no per-lane 64-bit address arithmetic).
+__device__ inline void copy16_async(const void* base, uint32_t off, void* lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(UF_LDS void*)lds_dst);
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off), "s"(sb) : "memory", "m0");
+}
 
 // 16-byte chunk swizzle of LDS row r (rows of D bytes): chunk c sits at c ^ swz(r), which
 // spreads both the 16-lane row-strided K reads and the 8-row transpose reads of V over
@@ -239,8 +248,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
       const uint8_t* vt_base = vbase + (int64_t)r0 * RB;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        copy16_async(kt_base + lane_off[i], kd + i * 1024);
-        copy16_async(vt_base + lane_off[i], vd + i * 1024);
+        copy16_async(kt_base, lane_off[i], kd + i * 1024);
+        copy16_async(vt_base, lane_off[i], vd + i * 1024);
       }
     } else {
 #pragma unroll
