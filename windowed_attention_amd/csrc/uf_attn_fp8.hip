@@ -46,9 +46,12 @@ __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ inline float sat(float x) { return fminf(fmaxf(x, -kMaxE4M3), kMaxE4M3); }
 
-// four floats -> one dword of four E4M3 codes (byte i = value i), nearest even
+// four floats -> one dword of four E4M3 codes (byte i = value i), nearest even.  The first
+// conversion writes the low half and keeps the high half of its `old` operand, which the
+// second conversion overwrites; a's own bits serve as `old`, so no register has to be
+// cleared first.
 __device__ inline int pack4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -317,8 +320,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, max_xor32(mx));
     const bool need = (m_new - m_run) * c2 > 8.f;  // lazy rescaling: P stays <= 2^8
     if (__ballot(need)) {
       const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c2) : 1.f;

@@ -40,6 +40,15 @@ __device__ inline int xcd_windowed(int b, int n) {
 // keys, which is the order the P.V product takes its B operand in.
 __device__ inline int rowperm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
+// Maximum of x over lanes l and l ^ 32 (the two halves of a wave).  One v_permlane32_swap
+// of x with itself leaves, in every lane, x of lane l in one result and x of lane l ^ 32 in
+// the other: lanes 0-31 keep their own value and receive lane l + 32's, lanes 32-63 receive
+// lane l - 32's and keep their own.
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Asynchronous copy of 16 bytes per lane from global memory into LDS (lane i's bytes land
 // at lds_dst + 16 i); completion is counted by vmcnt.
 __device__ inline void load_lds16(const void* src, void* lds_dst) {

@@ -279,8 +279,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, max_xor32(mx));
     const bool need = (m_new - m_run) * c2 > 8.f;  // lazy rescaling
     if (__ballot(need)) {
       const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c2) : 1.f;
