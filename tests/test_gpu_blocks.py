@@ -14,7 +14,7 @@ import torch
 import oracle
 import oracle.blocks as ob
 import oracle.fp8 as f8
-from synth import TILE, Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
+from synth import CONFIGS, TILE, Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
 from tests.gpu_util import assert_close, bits_of, f32_of, to_dev
 from tests.ring_model import RingModel
 from tests.test_gpu_topk import check_mask
@@ -120,4 +120,35 @@ def test_block_order_topk_mask():
     torch.cuda.synchronize()
     kk, _ = win.keys_values()
     check_mask(mask.cpu().numpy(), scores.cpu().numpy(), _perm(cfg, bf16_bits_to_f32(qb)), kk, 3, 1, "block-order")
+    cache.close()
+
+
+def test_block_order_2k_sampled():
+    """The 2K chunk held in block order at full size: 4 steps, sampled query tiles of steps 0
+    and 3 (tile t of the block order holds raster tokens order[128 t ...])."""
+    cfg = CONFIGS[4]
+    F = cfg.frames_per_step
+    order = ob.block_order(F, cfg.grid[0], cfg.grid[1])
+    cache = KVCache(cfg.n_kv_heads, cfg.head_dim, cfg.tokens_per_frame, cfg.window_frames, cfg.anchor_frames,
+                    block_grid=cfg.grid)
+    win = oracle.FrameListWindow(cfg.tokens_per_frame, cfg.window_frames, cfg.anchor_frames)
+    nqt = -(-cfg.q_tokens // TILE)
+    for s in range(cfg.steps):
+        qb, kb, vb = draw_step_tensors(cfg, s)
+        print(f"2k block order step {s}", flush=True)
+        cache.append(to_dev(kb), to_dev(vb), F)
+        win.append(bf16_bits_to_f32(kb)[order], bf16_bits_to_f32(vb)[order], F)
+        n_k = cache.window().n_keys
+        mask_np = make_block_mask(cfg.index, s, cfg.n_q_heads, cfg.q_tokens, n_k, cfg.mask_pct)
+        out = torch.empty_like(to_dev(qb))
+        cache.attn_step(to_dev(qb), out, torch.from_numpy(mask_np).to("cuda:0"))
+        if s not in (0, cfg.steps - 1):
+            continue
+        torch.cuda.synchronize()
+        tiles = sorted({0, nqt - 1, *np.random.default_rng(s).choice(np.arange(1, nqt - 1), 2, replace=False)})
+        rows = np.concatenate([np.arange(t * TILE, min((t + 1) * TILE, cfg.q_tokens)) for t in tiles])
+        kk, vv = win.keys_values()
+        ref = oracle.attend(bf16_bits_to_f32(qb)[order], kk, vv, mask_np, rows=rows)
+        got = f32_of(out)[order[rows]]
+        assert_close(got, ref, f"2k block order step {s}, tiles {tiles}")
     cache.close()

@@ -26,7 +26,8 @@ import torch
 
 import oracle
 import oracle.fp8 as f8
-from synth import TILE, Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
+from synth import CONFIGS, TILE, Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
+from tests import fp8_lut
 from tests.gpu_util import errors, f32_of, to_dev
 from tests.ring_model import RingModel
 from windowed_attention_amd import KVCache, uf
@@ -111,8 +112,8 @@ def run_fp8_stream(cfg, check_steps=None, tiles=None, scales=SCALES):
         q_d = to_dev(qb)
         print(f"{cfg.name} step {s}: fp8 append + attend", flush=True)
         cache.append(to_dev(kb), to_dev(vb), cfg.frames_per_step)
-        win.append(f8.dequantize(f8.quantize(bf16_bits_to_f32(kb), k_s), k_s),
-                   f8.dequantize(f8.quantize(bf16_bits_to_f32(vb), v_s), v_s), cfg.frames_per_step)
+        # oracle.fp8 quantization of bf16 inputs, tabulated over the 65536 bit patterns
+        win.append(fp8_lut.round_trip_bits(kb, k_s), fp8_lut.round_trip_bits(vb, v_s), cfg.frames_per_step)
         n_k = cache.window().n_keys
         mask_np = mask_d = None
         if cfg.mask_pct is not None:
@@ -127,7 +128,7 @@ def run_fp8_stream(cfg, check_steps=None, tiles=None, scales=SCALES):
         nqt = -(-cfg.q_tokens // TILE)
         sel_tiles = range(nqt) if tiles is None else sorted({0, nqt - 1, *range(1, nqt - 1, max(1, nqt // tiles))})
         rows = np.concatenate([np.arange(t * TILE, min((t + 1) * TILE, cfg.q_tokens)) for t in sel_tiles])
-        qq = f8.dequantize(f8.quantize(bf16_bits_to_f32(qb), q_s), q_s)
+        qq = fp8_lut.round_trip_bits(qb, q_s)
         kk, vv = win.keys_values()
         ref = oracle.attend(qq, kk, vv, mask_np, rows=rows)
         bound = _bound(qq, kk, vv, ref, mask_np, rows)
@@ -163,6 +164,11 @@ def test_fp8_forced_splits(monkeypatch):
 def test_fp8_1k_shape():
     cfg = Workload(3, "1k", "bf16", 12, 12, 128, (60, 104), 3, 6, 0, 2, 25)
     run_fp8_stream(cfg, check_steps=[0, 1], tiles=4)
+
+
+def test_fp8_2k_shape():
+    # the 2K chunk (90x156 tokens per frame, 15% mask) at full size, sampled query tiles
+    run_fp8_stream(CONFIGS[4], check_steps=[0, 3], tiles=3)
 
 
 def test_fp8_other_scales():
