@@ -373,11 +373,14 @@ uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mas
   const int n_hgrp = hq / hpw;
   const int64_t items = (int64_t)n_qblk * n_hgrp;
 
-  // Split the key range when the work items alone leave CUs idle.
+  // Split the key range when the work items alone leave CUs idle: as many splits as keep the
+  // whole grid resident at once (two work-groups per CU), at least 4 key tiles per split.
+  // One more split than that starts a second round of work-groups, which costs more than the
+  // shorter key ranges save (measured on the decoder shape: 3 splits 62 us, 4 splits 74 us).
   int splits = 1;
   const int cus = device_cu_count();
   if (items < 2 * cus) {
-    splits = (int)std::min<int64_t>((2 * cus + items - 1) / items, kMaxSplits);
+    splits = (int)std::min<int64_t>(std::max<int64_t>(1, (2 * cus) / items), kMaxSplits);
     splits = std::min(splits, std::max(1, n_kt / 4));
   }
   if (const char* e = getenv("UF_SPLITS")) {
