@@ -277,7 +277,8 @@ size_t uf_block_mask_workspace_bytes(const uf_kvcache_desc* desc, int32_t n_q_to
  * Rate and select key tiles for a step's queries q ([Nq, Hq, head_dim] bf16,
  * Hq a multiple of n_kv_heads, Nq <= the window's n_keys) against the keys
  * the cache exposes now (call it after the step's append, before
- * uf_attn_step); bf16 caches only (UF_ERR_UNSUPPORTED for an FP8 cache).
+ * uf_attn_step).  With an FP8 cache the keys are the stored codes times
+ * k_scale; q is used as given (bf16, not quantized).
  * Tiles are 128 tokens in query order and in key order; the
  * last tile of each may be partial and is averaged over its own tokens.
  *

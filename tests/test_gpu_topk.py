@@ -22,8 +22,9 @@ import torch
 
 import oracle
 from synth import TILE, Workload, bf16_bits_to_f32, draw_normal, draw_step_tensors, f32_to_bf16_bits
+from tests import fp8_lut
 from tests.gpu_util import assert_close, to_dev
-from windowed_attention_amd import KVCache
+from windowed_attention_amd import KVCache, uf
 
 pytestmark = pytest.mark.gpu
 
@@ -88,17 +89,24 @@ def check_mask(got_mask, got_scores, q, k, top_k, local, what):
     return exact, near
 
 
-def _stream(cfg, biased=False):
-    """Yield (step, q bits, cache, window keys) while streaming cfg's steps."""
+def _stream(cfg, biased=False, fp8_scales=None):
+    """Yield (step, q bits, cache, window keys) while streaming cfg's steps.  With fp8_scales
+    (q, k, v) the cache holds E4M3 codes and the oracle's window the dequantized values."""
     L, F, W, A = cfg.tokens_per_frame, cfg.frames_per_step, cfg.window_frames, cfg.anchor_frames
-    cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, W, A)
+    kw = {}
+    if fp8_scales is not None:
+        kw = dict(kv_dtype=uf.UF_FP8_E4M3, q_scale=fp8_scales[0], k_scale=fp8_scales[1], v_scale=fp8_scales[2])
+    cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, W, A, **kw)
     win = oracle.FrameListWindow(L, W, A)
     for s in range(cfg.steps):
         qb, kb, vb = draw_step_tensors(cfg, s)
         if biased:
             qb, kb = _biased(cfg, s, qb, kb)
         cache.append(to_dev(kb), to_dev(vb), F)
-        win.append(bf16_bits_to_f32(kb), bf16_bits_to_f32(vb), F)
+        if fp8_scales is None:
+            win.append(bf16_bits_to_f32(kb), bf16_bits_to_f32(vb), F)
+        else:
+            win.append(fp8_lut.round_trip_bits(kb, fp8_scales[1]), fp8_lut.round_trip_bits(vb, fp8_scales[2]), F)
         yield s, qb, cache, win
     cache.close()
 
@@ -114,9 +122,9 @@ def _biased(cfg, s, qb, kb):
     return add(qb, 4), add(kb, 5)
 
 
-def run_topk(cfg, top_k, local, steps=None, biased=False):
+def run_topk(cfg, top_k, local, steps=None, biased=False, fp8_scales=None):
     totals = [0, 0]
-    for s, qb, cache, win in _stream(cfg, biased):
+    for s, qb, cache, win in _stream(cfg, biased, fp8_scales):
         if steps is not None and s not in steps:
             continue
         q = to_dev(qb)
@@ -168,6 +176,20 @@ def test_topk_1k_shape():
 def test_topk_2k_shape_biased():
     cfg = Workload(4, "2k", "bf16", 12, 12, 128, (90, 156), 3, 6, 0, 2, None)
     exact, near = run_topk(cfg, top_k=97, local=1, steps=[1], biased=True)
+    assert exact > near
+
+
+@pytest.mark.parametrize("case", REDUCED[:2], ids=lambda c: c[0].name)
+def test_topk_from_fp8_cache(case):
+    """E4M3 keys (decoded exactly, times k_scale) against the oracle on the dequantized keys."""
+    cfg, top_k, local = case
+    exact, near = run_topk(cfg, top_k, local, biased=True, fp8_scales=(0.02, 0.03, 0.02))
+    assert exact >= 4 * near, (exact, near)
+
+
+def test_topk_from_fp8_cache_2k_shape():
+    cfg = Workload(4, "2k", "bf16", 12, 12, 128, (90, 156), 3, 6, 0, 2, None)
+    exact, near = run_topk(cfg, top_k=97, local=1, steps=[1], biased=True, fp8_scales=(0.02, 0.03, 0.02))
     assert exact > near
 
 

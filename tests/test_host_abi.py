@@ -308,16 +308,21 @@ def test_fp8_cache_description():
     uf.uf_kvcache_destroy(h.value)
 
 
-def test_mask_generation_rejects_fp8_cache():
+def test_mask_generation_validates_fp8_cache_like_bf16():
+    # an FP8 cache is accepted: the request is checked as for bf16 (here: a workspace one byte
+    # short), and the rejection happens before any launch
     d = fp8_desc(H=2, d=128, L=100, W=3)
     h = ctypes.c_void_p()
     assert LIB.uf_kvcache_create(ctypes.byref(d), ctypes.byref(h)) == uf.UF_OK
     try:
         uf.uf_kvcache_append(h.value, None, None, 2, uf.UF_APPEND_COMMIT_ONLY, 0)
         q = _tensor(100, 4, data=FAKE * 32)
+        need = uf.uf_block_mask_workspace_bytes(d, 100, 4)
+        assert need > 0
         got = LIB.uf_block_mask_topk(ctypes.byref(q), h.value, ctypes.byref(uf.uf_topk_params(2, 0)), FAKE * 512,
-                                     None, FAKE * 256, 1 << 20, None)
-        assert got == uf.UF_ERR_UNSUPPORTED, uf.uf_last_error()
+                                     None, FAKE * 256, need // 2, None)
+        assert got == uf.UF_ERR_INVALID_ARG, uf.uf_last_error()
+        assert "workspace" in uf.uf_last_error()
     finally:
         uf.uf_kvcache_destroy(h.value)
 

@@ -469,7 +469,6 @@ uf_status uf_block_mask_topk(const uf_tensor* q, const uf_kvcache* cache, const 
   if (!cache) return fail(UF_ERR_INVALID_ARG, "cache is NULL");
   if (!params) return fail(UF_ERR_INVALID_ARG, "params is NULL");
   const auto& d = cache->d;
-  if (d.kv_dtype != UF_BF16) return fail(UF_ERR_UNSUPPORTED, "mask generation reads bf16 caches only");
   uf_status s;
   if ((s = check_tensor(q, "q", d.head_dim)) != UF_OK) return s;
   if (q->n_heads % d.n_kv_heads != 0)
@@ -508,6 +507,8 @@ uf_status uf_block_mask_topk(const uf_tensor* q, const uf_kvcache* cache, const 
   p.q_stride_head = q->stride_head;
   p.k = (const uint16_t*)d.k_storage;
   p.kv_head_stride = rows_per_head(d) * d.head_dim;
+  p.k_fp8 = d.kv_dtype == UF_FP8_E4M3;
+  p.k_scale = d.k_scale;
   p.n_q = n_q;
   p.n_k = w.n_keys;
   p.n_q_heads = hq;

@@ -86,8 +86,10 @@ struct CombineParams {
 struct TopkParams {
   const uint16_t* q;
   int64_t q_stride_tok, q_stride_head;
-  const uint16_t* k;           // cache K storage base
-  int64_t kv_head_stride;      // rows_total * head_dim
+  const uint16_t* k;           // cache K storage base (bf16, or E4M3 bytes when k_fp8)
+  int64_t kv_head_stride;      // rows_total * head_dim (elements)
+  int32_t k_fp8;               // 1: K holds E4M3 codes, dequantized with k_scale
+  float k_scale;
   int32_t n_q;                 // query rows (the newest n_q of the n_k keys)
   int32_t n_k;                 // visible keys
   int32_t n_q_heads, n_kv_heads;

@@ -9,8 +9,9 @@
 // equal ratings going to the lower tile index.
 //
 //   pool_kernel   one work-group per (tile, head): fp32 sum of the tile's
-//                 bf16 rows, divided by the row count.  HBM-bound: it reads
-//                 q once and the visible K once.
+//                 bf16 rows (or E4M3 key rows, the mean then times the
+//                 cache's k scale), divided by the row count.  HBM-bound: it
+//                 reads q once and the visible K once.
 //   select_kernel one work-group per (head, 4 query tiles): the 4 x n_kb
 //                 ratings (fp32 fma chains over d in order) go to LDS as
 //                 order-preserving 32-bit keys; then one wave per row finds
@@ -68,6 +69,25 @@ __global__ void __launch_bounds__(kThreads) pool_kernel(TopkParams p) {
   for (int r = r0; r < n_rows; r += RP) {
     const int tok = tile * kTile + r;
     const int qtok = p.blk_h ? block_src_token(tok, p.blk_frames, p.blk_h, p.blk_w) : tok;
+    if (!is_q && p.k_fp8) {
+      // 8 E4M3 codes of channels 8c .. 8c + 7, decoded exactly to fp32
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(p.k) + (int64_t)head * p.kv_head_stride +
+                           key_row(p, tok) * D + c * 8;
+      const uint2 v = *reinterpret_cast<const uint2*>(src);
+      const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false);
+      const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true);
+      const auto e = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false);
+      const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
+      acc[0] += a[0];
+      acc[1] += a[1];
+      acc[2] += b[0];
+      acc[3] += b[1];
+      acc[4] += e[0];
+      acc[5] += e[1];
+      acc[6] += f[0];
+      acc[7] += f[1];
+      continue;
+    }
     const uint16_t* src = is_q ? p.q + (int64_t)qtok * p.q_stride_tok + (int64_t)head * p.q_stride_head
                                : p.k + (int64_t)head * p.kv_head_stride + key_row(p, tok) * D;
     const uint4 v = *reinterpret_cast<const uint4*>(src + c * 8);
@@ -87,7 +107,8 @@ __global__ void __launch_bounds__(kThreads) pool_kernel(TopkParams p) {
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < RP; ++r) s += part[r][threadIdx.x];
-    const float mean = s / (float)n_rows;
+    float mean = s / (float)n_rows;
+    if (!is_q && p.k_fp8) mean *= p.k_scale;
     if (is_q)
       p.qbar[((int64_t)head * p.n_qb + tile) * D + threadIdx.x] = mean;
     else  // channel-major, so that the selection kernel reads neighbouring key tiles side by side
