@@ -64,6 +64,14 @@ def test_fp8_append_codes_bit_exact(case):
         torch.cuda.synchronize()
         _same_codes(cache.k_storage, model.k, f"K codes, append {s}")
         _same_codes(cache.v_storage, model.v, f"V codes, append {s}")
+        if s == n // 2:  # re-write the newest append in place
+            _, kb2, vb2 = draw_step_tensors(cfg, s + 100, scale_q=1.0)
+            cache.append(to_dev(kb2), to_dev(vb2), F, uf.UF_APPEND_OVERWRITE_NEWEST)
+            model.overwrite_newest(f8.quantize(bf16_bits_to_f32(kb2), SCALES[1]).astype(np.uint16),
+                                   f8.quantize(bf16_bits_to_f32(vb2), SCALES[2]).astype(np.uint16))
+            torch.cuda.synchronize()
+            _same_codes(cache.k_storage, model.k, f"K codes, overwrite after append {s}")
+            _same_codes(cache.v_storage, model.v, f"V codes, overwrite after append {s}")
     cache.close()
 
 

@@ -13,15 +13,24 @@ import torch
 
 from synth import Workload, draw_step_tensors
 from tests.gpu_util import to_dev
-from windowed_attention_amd import KVCache
+from windowed_attention_amd import KVCache, uf
 
 pytestmark = pytest.mark.gpu
 
+CACHES = {
+    "bf16": {},
+    "fp8": dict(kv_dtype=uf.UF_FP8_E4M3, q_scale=0.02, k_scale=0.015, v_scale=0.02),
+    "block-order": dict(block_grid=(10, 20)),
+}
 
-def test_captured_step_replays_bit_exact():
-    cfg = Workload(50, "g-capture", "bf16", 4, 2, 128, (10, 20), 2, 4, 1, 5, None)
+
+@pytest.mark.parametrize("kind", list(CACHES))
+def test_captured_step_replays_bit_exact(kind):
+    # anchor of one step (2 frames of 10x20 tokens), window of 4 frames, GQA 2
+    cfg = Workload(50, "g-capture", "bf16", 4, 2, 128, (10, 20), 2, 4, 2, 5, None)
     F = cfg.frames_per_step
-    cache = KVCache(cfg.n_kv_heads, cfg.head_dim, cfg.tokens_per_frame, cfg.window_frames, cfg.anchor_frames)
+    cache = KVCache(cfg.n_kv_heads, cfg.head_dim, cfg.tokens_per_frame, cfg.window_frames, cfg.anchor_frames,
+                    **CACHES[kind])
     steps = [draw_step_tensors(cfg, s) for s in range(cfg.steps)]
     dev = [(to_dev(q), to_dev(k), to_dev(v)) for q, k, v in steps]
     last = cfg.steps - 1
