@@ -5,21 +5,12 @@ stored codes must equal the oracle's E4M3 codes, byte for byte, in the rows
 the ring model predicts.
 
 Attention: the oracle attends in float64 over the dequantized q, k and v (its
-plain definition).  The kernel differs from it by rounding the probabilities
-to E4M3 for the P.V product (and the row sums it divides by).  With weights p
-normalised to a maximum of 1, E4M3 rounding moves each weight by at most
-e_j = max(2^-4 p_j, 2^-10) (half an ulp: relative 2^-4 for normal codes,
-absolute 2^-10 below 2^-6; the kernel's running reference max can only be
-smaller than the true one, which only lowers the relative cut-off).  With the
-same rounded weights in numerator and denominator,
-    |out - ref| <= sum_j e_j |v_j - ref| / (sum_j p_j - sum_j e_j)
-               <= (sum_j e_j |v_j| + |ref| sum_j e_j) / (sum_j p_j - sum_j e_j),
-plus the bf16 rounding of the output (2^-9 |ref|).  The tests compute that
-bound per output element from the oracle's weights and require every element
-within it (and print how much of it was used).
+plain definition).  The kernel differs from it by rounding the probabilities to
+E4M3 for the P.V product and the output to bf16; tests/fp8_bound.py derives a
+per-element bound for that (and tests/test_fp8_bound.py checks the bound on an
+emulation of the kernel's arithmetic).  Every output element must lie within it;
+the tests print how much of it was used.
 """
-import math
-
 import numpy as np
 import pytest
 import torch
@@ -28,6 +19,7 @@ import oracle
 import oracle.fp8 as f8
 from synth import CONFIGS, TILE, Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
 from tests import fp8_lut
+from tests.fp8_bound import bound as _bound
 from tests.gpu_util import errors, f32_of, to_dev
 from tests.ring_model import RingModel
 from windowed_attention_amd import KVCache, uf
@@ -83,30 +75,6 @@ def _same_codes(storage, want, what):
         print(f"  {what}: head {h} row {r} ch {c}: got 0x{g:02x} ({f8.e4m3_decode(np.array([g]))[0]}), "
               f"want 0x{w:02x} ({f8.e4m3_decode(np.array([w]))[0]})", flush=True)
     assert len(bad) == 0, f"{what}: {len(bad)} codes differ"
-
-
-def _bound(q, k, v, ref, mask, rows):
-    """Per-element bound of the E4M3 probability rounding (see the module docstring)."""
-    n_q_heads, d = q.shape[1], q.shape[2]
-    group = n_q_heads // k.shape[1]
-    out = np.zeros_like(ref)
-    row_tile = rows // TILE
-    for h in range(n_q_heads):
-        kh, vh = k[:, h // group, :], v[:, h // group, :]
-        for qt in np.unique(row_tile):
-            sel = np.nonzero(row_tile == qt)[0]
-            keys = np.ones(k.shape[0], dtype=bool)
-            if mask is not None:
-                keys = np.repeat(mask[0 if mask.shape[0] == 1 else h, qt] != 0, TILE)[:k.shape[0]]
-            if not keys.any():
-                continue
-            s = q[rows[sel], h, :] @ kh[keys].T / math.sqrt(d)
-            p = np.exp(s - s.max(axis=1, keepdims=True))
-            e = np.maximum(2.0 ** -4 * p, 2.0 ** -10)
-            # sum_j e_j |v_j - ref| <= sum_j e_j |v_j| + |ref| sum_j e_j
-            num = e @ np.abs(vh[keys]) + np.abs(ref[sel, h, :]) * e.sum(axis=1)[:, None]
-            out[sel, h, :] = num / (p.sum(axis=1) - e.sum(axis=1))[:, None]
-    return out + 2.0 ** -9 * np.abs(ref) + 1e-6
 
 
 def run_fp8_stream(cfg, check_steps=None, tiles=None, scales=SCALES):

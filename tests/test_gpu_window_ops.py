@@ -18,7 +18,7 @@ import oracle.blocks as ob
 from synth import Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
 from tests import fp8_lut
 from tests.gpu_util import assert_close, f32_of, to_dev
-from tests.test_gpu_fp8 import _bound
+from tests.fp8_bound import bound as _bound
 from windowed_attention_amd import KVCache, uf
 
 pytestmark = pytest.mark.gpu
