@@ -147,6 +147,13 @@ def test_fp8_2k_shape():
     run_fp8_stream(CONFIGS[4], check_steps=[0, 3], tiles=3)
 
 
+def test_fp8_decoder_shape():
+    # the decoder step at full size: 12 query heads on 3 KV heads, 1560 tokens per frame, window of
+    # 2 frames; few enough work items that the key range is split (combine kernel)
+    cfg = Workload(2, "decoder", "bf16", 12, 3, 128, (30, 52), 1, 2, 0, 5, None)
+    run_fp8_stream(cfg, check_steps=[0, 1, 4])
+
+
 def test_fp8_other_scales():
     # a coarser q scale and a finer v scale
     run_fp8_stream(Workload(65, "f8-scales", "bf16", 2, 2, 128, (8, 25), 1, 3, 0, 4, None), scales=(0.05, 0.01, 0.005))
