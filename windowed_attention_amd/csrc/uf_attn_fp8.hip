@@ -107,18 +107,28 @@ __global__ void __launch_bounds__(kThreads) append_fp8_kernel(AppendFp8Params p)
 // take it for an LDS store that every later LDS read must wait for, which would hold the
 // reads of the current tile until the next tile's copy has landed.  The callers wait for
 // the copies themselves (s_waitcnt vmcnt(0) before the barrier that publishes a tile).
+// The LDS address goes in M0, which the compiler reserves: each statement saves M0 in a
+// scratch SGPR and restores it after the instruction has issued.
 __device__ inline void copy16_async(const void* src, void* lds_dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(UF_LDS void*)lds_dst);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(UF_LDS void*)lds_dst);
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds), "v"(src)
+               : "memory");
 }
 // The same from a wave-uniform base plus a 32-bit per-lane byte offset (the scalar-base
 // form of the instruction: no per-lane 64-bit address arithmetic).
 __device__ inline void copy16_async(const void* base, uint32_t off, void* lds_dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(UF_LDS void*)lds_dst);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(UF_LDS void*)lds_dst);
   const uint64_t b = (uint64_t)(uintptr_t)base;
   const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off), "s"(sb) : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds), "v"(off), "s"(sb)
+               : "memory");
 }
 
 // 16-byte chunk swizzle of LDS row r (rows of D bytes): chunk c sits at c ^ swz(r), which
