@@ -27,7 +27,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from synth import CONFIGS, TILE, bf16_bits_to_f32, draw_step_tensors, make_block_mask  # noqa: E402
+from synth import WORKLOADS, TILE, bf16_bits_to_f32, draw_step_tensors, make_block_mask  # noqa: E402
 
 METRIC = "attention TFLOP/s (% bf16 MFMA peak) + frames/s at 1K and 2K chunk shapes"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 FLOP/clk/CU)
@@ -336,7 +336,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="2k", choices=[c.name for c in CONFIGS])
+    ap.add_argument("--workload", default="2k", choices=[c.name for c in WORKLOADS])
     ap.add_argument("--also", default="1k", help="comma-separated extra workloads reported under 'also' ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true", help="skip the block-mask generation leg")
@@ -348,7 +348,7 @@ def main():
                          "against which profiler byte counters are scaled")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -363,11 +363,11 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: 3 copies of {args.copy_calibration_mib} MiB")
         del src, dst
-    cfg = {c.name: c for c in CONFIGS}[args.workload]
+    cfg = {c.name: c for c in WORKLOADS}[args.workload]
     main_r = run_workload(cfg, args.warmup, args.steps)
     also = {}
     for name in [n for n in args.also.split(",") if n and n != cfg.name]:
-        r = run_workload({c.name: c for c in CONFIGS}[name], args.warmup, args.steps)
+        r = run_workload({c.name: c for c in WORKLOADS}[name], args.warmup, args.steps)
         also[name] = summary(r)
         del r
     fp8 = None

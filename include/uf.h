@@ -59,7 +59,7 @@ typedef enum uf_status {
   UF_ERR_CAPACITY = -4,     /* more frames than the ring holds, or index ranges beyond 2^31 */
   UF_ERR_STATE = -5,        /* call not valid in the cache's current state */
   UF_ERR_HIP = -6,          /* the HIP runtime reported an error (message in uf_last_error) */
-  UF_ERR_UNSUPPORTED = -7   /* valid request this build does not implement (e.g. head_dim) */
+  UF_ERR_UNSUPPORTED = -7   /* valid request the library does not implement (e.g. head_dim) */
 } uf_status;
 
 typedef enum uf_dtype {

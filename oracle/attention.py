@@ -1,6 +1,6 @@
 """softmax(Q K^T / sqrt(d)) V in float64 (oracle, test infrastructure).
 
-Definition followed (BASELINE's stated operation, plus the pages):
+Definition followed (the operation the pages name, with these readings):
   * Scores are q . k / sqrt(d), softmax over the visible keys, output the
     softmax-weighted sum of values.  The 1/sqrt(d) scale is the standard
     attention scale; the pages name the operation without restating it.

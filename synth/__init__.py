@@ -4,7 +4,8 @@ This package only draws numbers and shapes them: it holds none of the
 attention arithmetic, no window bookkeeping and no reference results.
 """
 from .workloads import (
-    CONFIGS,
+    WORKLOAD,
+    WORKLOADS,
     Workload,
     TILE,
     draw_normal,
@@ -16,7 +17,8 @@ from .workloads import (
 )
 
 __all__ = [
-    "CONFIGS",
+    "WORKLOAD",
+    "WORKLOADS",
     "Workload",
     "TILE",
     "draw_normal",

@@ -1,7 +1,7 @@
 """Workload shapes and seeded generators for the streaming-attention path.
 
 Every tensor is drawn from numpy's PCG64 seeded with
-``SeedSequence([config_index, step, tensor_id])`` (tensor ids: q=0, k=1,
+``SeedSequence([workload_index, step, tensor_id])`` (tensor ids: q=0, k=1,
 v=2, block mask=3), as float32 standard normals in token-major layout
 ``[tokens, heads, head_dim]``.  The HIP side receives the bf16 (round to
 nearest even) encoding of those draws and the oracle receives the very same
@@ -60,7 +60,7 @@ class Workload:
         return self.frames_per_step * self.tokens_per_frame
 
 
-CONFIGS = [
+WORKLOADS = [
     Workload(0, "tiny", "f32", 2, 2, 64, (8, 8), 1, 3, 0, 6, None),
     Workload(1, "480p", "bf16", 12, 12, 128, (30, 52), 3, 9, 3, 8, None),
     Workload(2, "decoder", "bf16", 12, 3, 128, (30, 52), 1, 2, 0, 120, None),
@@ -69,15 +69,16 @@ CONFIGS = [
     Workload(5, "decoder-xl", "bf16", 24, 3, 64, (45, 80), 1, 2, 0, 24, None),
     Workload(6, "refine-xl", "bf16", 24, 3, 64, (45, 80), 4, 8, 0, 6, None),
 ]
+WORKLOAD = {w.name: w for w in WORKLOADS}  # by name
 
 
-def _rng(config_index: int, step: int, tensor_id: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([config_index, step, tensor_id])))
+def _rng(workload_index: int, step: int, tensor_id: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([workload_index, step, tensor_id])))
 
 
-def draw_normal(config_index: int, step: int, tensor_id: int, shape: Sequence[int]) -> np.ndarray:
+def draw_normal(workload_index: int, step: int, tensor_id: int, shape: Sequence[int]) -> np.ndarray:
     """float32 standard normals of `shape` from the (config, step, tensor) stream."""
-    return _rng(config_index, step, tensor_id).standard_normal(tuple(shape), dtype=np.float32)
+    return _rng(workload_index, step, tensor_id).standard_normal(tuple(shape), dtype=np.float32)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -124,7 +125,7 @@ def diagonal_tiles(q_tile: int, n_q: int, n_k: int, tile: int = TILE) -> list:
     return list(range(lo // tile, (hi - 1) // tile + 1))
 
 
-def make_block_mask(config_index: int, step: int, n_heads: int, n_q: int, n_k: int,
+def make_block_mask(workload_index: int, step: int, n_heads: int, n_q: int, n_k: int,
                     pct: int, tile: int = TILE) -> np.ndarray:
     """Seeded block mask, uint8 [n_heads, ceil(n_q/tile), ceil(n_k/tile)] (1 = keep).
 
@@ -135,7 +136,7 @@ def make_block_mask(config_index: int, step: int, n_heads: int, n_q: int, n_k: i
     """
     nqb = -(-n_q // tile)
     nkb = -(-n_k // tile)
-    rng = _rng(config_index, step, TENSOR_MASK)
+    rng = _rng(workload_index, step, TENSOR_MASK)
     mask = np.zeros((n_heads, nqb, nkb), dtype=np.uint8)
     target = (pct * nkb + 50) // 100
     for h in range(n_heads):

@@ -14,7 +14,7 @@ import torch
 import oracle
 import oracle.blocks as ob
 import oracle.fp8 as f8
-from synth import CONFIGS, TILE, Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
+from synth import WORKLOAD, TILE, Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
 from tests.gpu_util import assert_close, bits_of, f32_of, to_dev
 from tests.ring_model import RingModel
 from tests.test_gpu_topk import check_mask
@@ -126,7 +126,7 @@ def test_block_order_topk_mask():
 def test_block_order_2k_sampled():
     """The 2K chunk held in block order at full size: 4 steps, sampled query tiles of steps 0
     and 3 (tile t of the block order holds raster tokens order[128 t ...])."""
-    cfg = CONFIGS[4]
+    cfg = WORKLOAD["2k"]
     F = cfg.frames_per_step
     order = ob.block_order(F, cfg.grid[0], cfg.grid[1])
     cache = KVCache(cfg.n_kv_heads, cfg.head_dim, cfg.tokens_per_frame, cfg.window_frames, cfg.anchor_frames,

@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import oracle.fp8 as f8
-from synth import CONFIGS, TILE, Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
+from synth import WORKLOAD, TILE, Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
 from tests import fp8_lut
 from tests.fp8_bound import bound as _bound
 from tests.gpu_util import errors, f32_of, to_dev
@@ -144,7 +144,7 @@ def test_fp8_1k_shape():
 
 def test_fp8_2k_shape():
     # the 2K chunk (90x156 tokens per frame, 15% mask) at full size, sampled query tiles
-    run_fp8_stream(CONFIGS[4], check_steps=[0, 3], tiles=3)
+    run_fp8_stream(WORKLOAD["2k"], check_steps=[0, 3], tiles=3)
 
 
 def test_fp8_decoder_shape():

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from synth import (CONFIGS, TILE, Workload, bf16_bits_to_f32, draw_normal, draw_step_tensors, f32_to_bf16_bits,
+from synth import (WORKLOAD, TILE, Workload, bf16_bits_to_f32, draw_normal, draw_step_tensors, f32_to_bf16_bits,
                    make_block_mask)
 from tests.gpu_util import assert_close, bits_of, errors, f32_of, to_dev
 from windowed_attention_amd import KVCache, uf
@@ -91,33 +91,33 @@ def run_stream(cfg: Workload, check_steps=None, tiles=None, shared_mask=False, s
 
 def test_tiny_all_steps():
     # bf16 path on the tiny workload; also within 1e-2 rel-L2 of the oracle on the raw float32 draws
-    run_stream(CONFIGS[0], raw_fp32_oracle=True)
+    run_stream(WORKLOAD["tiny"], raw_fp32_oracle=True)
 
 
 def test_480p_anchor_stream():
-    run_stream(CONFIGS[1], check_steps=[0, 1, 3, 4, 7], tiles=6)
+    run_stream(WORKLOAD["480p"], check_steps=[0, 1, 3, 4, 7], tiles=6)
 
 
 def test_decoder_gqa_stream():
-    run_stream(CONFIGS[2], check_steps=[0, 1, 2, 3, 60, 119], tiles=None)
+    run_stream(WORKLOAD["decoder"], check_steps=[0, 1, 2, 3, 60, 119], tiles=None)
 
 
 def test_1k_masked_stream():
-    run_stream(CONFIGS[3], tiles=6)
+    run_stream(WORKLOAD["1k"], tiles=6)
 
 
 def test_2k_masked_stream():
-    run_stream(CONFIGS[4], tiles=5)
+    run_stream(WORKLOAD["2k"], tiles=5)
 
 
 def test_decoder_xl_stream():
     # head_dim 64, 24 query heads over 3 KV heads (8 per group), per-frame steps
-    run_stream(CONFIGS[5], check_steps=[0, 1, 2, 23], tiles=6)
+    run_stream(WORKLOAD["decoder-xl"], check_steps=[0, 1, 2, 23], tiles=6)
 
 
 def test_refine_xl_stream():
     # temporal refinement: 4-frame steps over an 8-frame window, head_dim 64, GQA 8
-    run_stream(CONFIGS[6], check_steps=[0, 1, 2, 5], tiles=5)
+    run_stream(WORKLOAD["refine-xl"], check_steps=[0, 1, 2, 5], tiles=5)
 
 
 # ---------------------------------------------------------------------------------------------

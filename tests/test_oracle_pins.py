@@ -17,7 +17,7 @@ import torch
 import oracle
 import oracle.attention as oatt
 import oracle.window as owin
-from synth import CONFIGS, draw_normal, f32_to_bf16_bits, bf16_bits_to_f32, make_block_mask, diagonal_tiles
+from synth import WORKLOADS, draw_normal, f32_to_bf16_bits, bf16_bits_to_f32, make_block_mask, diagonal_tiles
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -74,7 +74,7 @@ def check_identical_keys_give_mean_value():
 def check_window_tables():
     """The frame-list model reproduces the hand-derived window tables (tests/golden/windows.json)."""
     table = json.load(open(os.path.join(GOLDEN, "windows.json")))
-    for cfg in CONFIGS:
+    for cfg in WORKLOADS:
         t = table[cfg.name]
         F, L = t["frames_per_step"], t["tokens_per_frame"]
         assert (F, L) == (cfg.frames_per_step, cfg.tokens_per_frame)
@@ -90,7 +90,7 @@ def check_uniform_queries_reveal_window():
     counts the visible keys of every frame: it must be L/N_k on exactly the
     visible frames of the golden table."""
     table = json.load(open(os.path.join(GOLDEN, "windows.json")))
-    for cfg in CONFIGS:
+    for cfg in WORKLOADS:
         t = table[cfg.name]
         L, F = 4, cfg.frames_per_step          # reduced tokens per frame, same frame logic
         n_steps = len(t["units"])
