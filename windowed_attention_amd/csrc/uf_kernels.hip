@@ -361,33 +361,36 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------------------
 // Split-KV combine: out = sum_s w_s O_s / sum_s w_s l_s, w_s = 2^(m_s - max_s m_s).
-// One wave per (query, head) row.
+// D / 8 lanes per (query, head) row, 8 channels each: two 16-byte loads per split and one
+// 16-byte store per lane.
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) combine_kernel(CombineParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  constexpr int LPR = D / 8;              // lanes per row
+  constexpr int RPW = kThreads / LPR;     // rows per work-group
+  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / LPR;
+  const int c0 = 8 * (threadIdx.x % LPR);
   const int64_t rows = (int64_t)p.n_q * p.n_q_heads;
   if (row >= rows) return;
   float mmax = -INFINITY;
   for (int s = 0; s < p.splits; ++s) mmax = fmaxf(mmax, p.ws_ml[2 * (s * rows + row)]);
-  constexpr int PER = D / 64;  // d values per lane
-  float acc[PER] = {};
+  f32x4 a0 = {}, a1 = {};
   float l = 0.f;
   if (mmax != -INFINITY) {
     for (int s = 0; s < p.splits; ++s) {
-      const float w = __builtin_amdgcn_exp2f(p.ws_ml[2 * (s * rows + row)] - mmax);
-      l += w * p.ws_ml[2 * (s * rows + row) + 1];
-      const float* src = p.ws_o + (s * rows + row) * D;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += w * src[lane * PER + i];
+      const float* ml = p.ws_ml + 2 * (s * rows + row);
+      const float w = __builtin_amdgcn_exp2f(ml[0] - mmax);
+      l += w * ml[1];
+      const f32x4* src = reinterpret_cast<const f32x4*>(p.ws_o + (s * rows + row) * D + c0);
+      a0 += w * src[0];
+      a1 += w * src[1];
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const int qi = (int)(row / p.n_q_heads), head = (int)(row % p.n_q_heads);
-  __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)qi * p.o_stride_tok + (int64_t)head * p.o_stride_head;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) op[lane * PER + i] = (__bf16)(acc[i] * inv);
+  __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)qi * p.o_stride_tok + (int64_t)head * p.o_stride_head + c0;
+  const f32x8 x = {a0[0] * inv, a0[1] * inv, a0[2] * inv, a0[3] * inv, a1[0] * inv, a1[1] * inv, a1[2] * inv, a1[3] * inv};
+  *reinterpret_cast<bf16x8*>(op) = __builtin_convertvector(x, bf16x8);
 }
 
 }  // namespace
@@ -411,7 +414,8 @@ hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t strea
 
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream) {
   const int64_t rows = (int64_t)p.n_q * p.n_q_heads;
-  const int blocks = (int)((rows + 3) / 4);
+  const int64_t rows_per_wg = kThreads / (head_dim / 8);
+  const int blocks = (int)((rows + rows_per_wg - 1) / rows_per_wg);
   if (head_dim == 128)
     hipLaunchKernelGGL(combine_kernel<128>, dim3(blocks), dim3(kThreads), 0, stream, p);
   else
