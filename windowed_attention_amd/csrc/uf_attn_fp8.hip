@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "uf_attn_walk.h"
 #include "uf_device.h"
 #include "uf_internal.h"
 
@@ -161,18 +162,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
   const int l32 = lane & 31, half = lane >> 5;
   const int rb = wave;
 
-  const int item = xcd_windowed(blockIdx.x, gridDim.x);
-  const int qblk = item % p.n_qblk;
-  const int rest = item / p.n_qblk;
-  const int split = rest % p.splits;
-  const int hgrp = rest / p.splits;
-  const int waves_per_head = 4 / p.heads_per_wg;
-  const int q0 = qblk * (kTile / p.heads_per_wg);
-  const int kvh = (hgrp * p.heads_per_wg) / p.group;
-  const int q_tile = q0 / kTile;
-  const int head = hgrp * p.heads_per_wg + rb / waves_per_head;
-  const int qi = q0 + (rb % waves_per_head) * 32 + l32;
-  const int qt = p.blk_h && qi < p.n_q ? block_src_token(qi, p.blk_frames, p.blk_h, p.blk_w) : qi;
+  const AttnItem it = attn_item(p, blockIdx.x, gridDim.x, rb, l32);
+  const int head = it.head, kvh = it.kvh, qi = it.qi, qt = it.qt;
 
   // ---- Q^T fragments (B operand): lane (query, half) holds channels 64c + 32 half .. +31
   i32x8 qf[NCH];
@@ -202,38 +193,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
   const float c2 = p.scale_log2;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) + (int64_t)kvh * p.kv_head_stride;
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) + (int64_t)kvh * p.kv_head_stride;
-  auto key_row = [&](int j) -> int {
-    if (j < p.anchor_keys) return j;
-    int r = j - p.anchor_keys + p.ring_rot;
-    if (r >= p.ring_cap) r -= p.ring_cap;
-    return p.ring_base + r;
-  };
-  const int nkt = (p.n_k + kTile - 1) / kTile;
-  const int kt_lo = (int)(((int64_t)split * nkt) / p.splits);
-  const int kt_hi = (int)(((int64_t)(split + 1) * nkt) / p.splits);
-  const uint8_t* mrow = nullptr;
-  if (p.mask) {
-    const int mh = p.mask_heads == 1 ? 0 : head;
-    mrow = p.mask + mh * p.mask_stride_head + (int64_t)q_tile * p.mask_stride_q;
-  }
-  int w0 = kt_lo - 64;
-  uint64_t bits = 0;
-  auto next_tile = [&]() -> int {
-    while (bits == 0) {
-      w0 += 64;
-      if (w0 >= kt_hi) return -1;
-      if (mrow) {
-        const int kt = w0 + lane;
-        bits = __ballot(kt < kt_hi && mrow[kt] != 0);
-      } else {
-        const int n = min(64, kt_hi - w0);
-        bits = n == 64 ? ~0ull : ((1ull << n) - 1ull);
-      }
-    }
-    const int kt = w0 + __builtin_ctzll(bits);
-    bits &= bits - 1;
-    return __builtin_amdgcn_readfirstlane(kt);
-  };
+  KeyTiles tiles(p, it);  // the kept key tiles, ascending
 
   uint32_t lane_off[NLD];
 #pragma unroll
@@ -246,16 +206,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
     const int nvalid = min(kTile, p.n_k - j0);
     char* kd = smem + buf * BUF_B + wave * NLD * 1024;
     char* vd = kd + TILE_B;
-    int r0 = -1;
-    if (nvalid == kTile) {
-      if (j0 + kTile <= p.anchor_keys) {
-        r0 = j0;
-      } else if (j0 >= p.anchor_keys) {
-        int r = j0 - p.anchor_keys + p.ring_rot;
-        if (r >= p.ring_cap) r -= p.ring_cap;
-        if (r + kTile <= p.ring_cap) r0 = p.ring_base + r;
-      }
-    }
+    const int r0 = contiguous_tile_rows(p, kt);
     if (r0 >= 0) {
       const uint8_t* kt_base = kbase + (int64_t)r0 * RB;
       const uint8_t* vt_base = vbase + (int64_t)r0 * RB;
@@ -269,7 +220,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
       for (int i = 0; i < NLD; ++i) {
         const int row = (wave * NLD + i) * RPI + lane / CPR;
         const int chunk = (lane % CPR) ^ swz8<D>(row);
-        const int64_t off = (int64_t)key_row(j0 + min(row, nvalid - 1)) * RB + chunk * 16;
+        const int64_t off = (int64_t)key_row(p, j0 + min(row, nvalid - 1)) * RB + chunk * 16;
         copy16_async(kbase + off, kd + i * 1024);
         copy16_async(vbase + off, vd + i * 1024);
       }
@@ -373,13 +324,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
   // Tile i sits in buffer i % 2.  The barrier at the top of step i publishes tile i (every
   // wave has waited for its own copies) and also shows that every wave has finished tile
   // i - 1, whose buffer the copy of tile i + 1 then overwrites.
-  int kt = next_tile();
+  int kt = tiles.next(lane);
   int buf = 0;
   if (kt >= 0) issue(kt, 0);
   while (kt >= 0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int kn = next_tile();
+    const int kn = tiles.next(lane);
     if (kn >= 0) issue(kn, buf ^ 1);
     compute(min(kTile, p.n_k - kt * kTile), buf);
     kt = kn;
@@ -400,7 +351,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g + 4 * half) = __builtin_convertvector(x, bf16x4);
       }
   } else {
-    const int64_t row = ((int64_t)split * p.n_q + qt) * p.n_q_heads + head;
+    const int64_t row = ((int64_t)it.split * p.n_q + qt) * p.n_q_heads + head;
     float* wo = p.ws_o + row * D;
 #pragma unroll
     for (int db = 0; db < ND; ++db)

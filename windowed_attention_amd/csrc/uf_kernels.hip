@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "uf_attn_walk.h"
 #include "uf_device.h"
 #include "uf_internal.h"
 
@@ -118,19 +119,8 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
   const int rb = wave;  // row block
 
   // ---- work item
-  const int item = xcd_windowed(blockIdx.x, gridDim.x);
-  const int qblk = item % p.n_qblk;
-  const int rest = item / p.n_qblk;
-  const int split = rest % p.splits;
-  const int hgrp = rest / p.splits;
-  const int waves_per_head = 4 / p.heads_per_wg;
-  const int q0 = qblk * (kTile / p.heads_per_wg);
-  const int kvh = (hgrp * p.heads_per_wg) / p.group;
-  const int q_tile = q0 / kTile;  // block-mask row
-  const int head = hgrp * p.heads_per_wg + rb / waves_per_head;
-  const int qi = q0 + (rb % waves_per_head) * 32 + l32;  // this lane's query row
-  // its token in q and out (differs from qi when the step is held in block order)
-  const int qt = p.blk_h && qi < p.n_q ? block_src_token(qi, p.blk_frames, p.blk_h, p.blk_w) : qi;
+  const AttnItem it = attn_item(p, blockIdx.x, gridDim.x, rb, l32);
+  const int head = it.head, kvh = it.kvh, qi = it.qi, qt = it.qt;
 
   // ---- Q^T fragments (B operand), in registers for the whole key range
   bf16x8 qf[NC];
@@ -153,40 +143,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
   const float c2 = p.scale_log2;
   const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)kvh * p.kv_head_stride;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)kvh * p.kv_head_stride;
-  // storage row of logical key j
-  auto key_row = [&](int j) -> int {
-    if (j < p.anchor_keys) return j;
-    int r = j - p.anchor_keys + p.ring_rot;
-    if (r >= p.ring_cap) r -= p.ring_cap;
-    return p.ring_base + r;
-  };
-  const int nkt = (p.n_k + kTile - 1) / kTile;
-  const int kt_lo = (int)(((int64_t)split * nkt) / p.splits);
-  const int kt_hi = (int)(((int64_t)(split + 1) * nkt) / p.splits);
-  const uint8_t* mrow = nullptr;
-  if (p.mask) {
-    const int mh = p.mask_heads == 1 ? 0 : head;  // heads_per_wg > 1 only with a shared mask
-    mrow = p.mask + mh * p.mask_stride_head + (int64_t)q_tile * p.mask_stride_q;
-  }
-  // kept key tiles in ascending order: 64 at a time from a wave ballot over the mask row
-  int w0 = kt_lo - 64;
-  uint64_t bits = 0;
-  auto next_tile = [&]() -> int {
-    while (bits == 0) {
-      w0 += 64;
-      if (w0 >= kt_hi) return -1;
-      if (mrow) {
-        const int kt = w0 + lane;
-        bits = __ballot(kt < kt_hi && mrow[kt] != 0);
-      } else {
-        const int n = min(64, kt_hi - w0);
-        bits = n == 64 ? ~0ull : ((1ull << n) - 1ull);
-      }
-    }
-    const int kt = w0 + __builtin_ctzll(bits);
-    bits &= bits - 1;
-    return __builtin_amdgcn_readfirstlane(kt);  // the same on every lane
-  };
+  KeyTiles tiles(p, it);  // the kept key tiles, ascending
 
   // K and V of tile kt -> LDS (asynchronous; completion via vmcnt).  Lane
   // element offsets for a tile whose 128 keys are 128 consecutive storage
@@ -203,16 +160,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
     const int nvalid = min(kTile, p.n_k - j0);
     char* kd = smem + wave * NLD * 1024;
     char* vd = kd + TILE_B;
-    int r0 = -1;
-    if (nvalid == kTile) {
-      if (j0 + kTile <= p.anchor_keys) {
-        r0 = j0;
-      } else if (j0 >= p.anchor_keys) {
-        int r = j0 - p.anchor_keys + p.ring_rot;
-        if (r >= p.ring_cap) r -= p.ring_cap;
-        if (r + kTile <= p.ring_cap) r0 = p.ring_base + r;
-      }
-    }
+    const int r0 = contiguous_tile_rows(p, kt);
     if (r0 >= 0) {
       const __bf16* kt_base = kbase + (int64_t)r0 * D;
       const __bf16* vt_base = vbase + (int64_t)r0 * D;
@@ -226,7 +174,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
       for (int i = 0; i < NLD; ++i) {
         const int row = (wave * NLD + i) * RPI + lane / CPR;
         const int chunk = (lane % CPR) ^ swz<D>(row);
-        const int64_t off = (int64_t)key_row(j0 + min(row, nvalid - 1)) * D + chunk * 8;
+        const int64_t off = (int64_t)key_row(p, j0 + min(row, nvalid - 1)) * D + chunk * 8;
         load_lds16(kbase + off, kd + i * 1024);
         load_lds16(vbase + off, vd + i * 1024);
       }
@@ -321,7 +269,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
   };
 
   // ---- main loop: the other work-group on this CU computes while this one loads
-  for (int kt = next_tile(); kt >= 0; kt = next_tile()) {
+  for (int kt = tiles.next(lane); kt >= 0; kt = tiles.next(lane)) {
     issue(kt);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // the tile is in LDS for every wave
@@ -343,7 +291,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g + 4 * half) = __builtin_convertvector(x, bf16x4);
       }
   } else {
-    const int64_t row = ((int64_t)split * p.n_q + qt) * p.n_q_heads + head;
+    const int64_t row = ((int64_t)it.split * p.n_q + qt) * p.n_q_heads + head;
     float* wo = p.ws_o + row * D;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
