@@ -36,6 +36,7 @@ PEAK_FP8_TFLOPS = 5033.2    # MI355X dense FP8 MFMA (twice the bf16 rate)
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_2k_traffic.md")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_kernel_2k_1k_mfma_counters.md")
 KERNEL_SOURCE = os.path.join(ROOT, "windowed_attention_amd", "csrc", "uf_kernels.hip")
 
 
@@ -52,6 +53,23 @@ def measured_traffic(workload):
     if not m or not t or m.group(1) != src:
         return None
     return int(t.group(1))
+
+
+def profiled_clock(workload):
+    """Clock (GHz) the chip held under the attention kernel in the committed MFMA counter
+    summary (GRBM_GUI_ACTIVE per XCD over the dispatch time), or None when that summary was
+    taken on a different kernel source."""
+    try:
+        text = open(COUNTERS_FILE).read()
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"sha256 `([0-9a-f]{64})`", text)
+    row = re.search(r"^\| %s \|(.*)$" % re.escape(workload), text, re.M)
+    if not m or not row or m.group(1) != src:
+        return None
+    cells = [c.strip() for c in row.group(1).split("|")]
+    return float(cells[6])  # dispatch, MFMA FLOPs, executed FLOPs, MFMA, VALU, exp, clock
 
 
 def log(msg):
@@ -397,6 +415,7 @@ def main():
     s = summary(main_r)
     traffic_bytes = measured_traffic(cfg.name)
     traffic_gbs = None if traffic_bytes is None else round(traffic_bytes / (main_r["attn_ms"] * 1e-3) / 1e9, 1)
+    clock = profiled_clock(cfg.name)
     line = {
         "metric": METRIC,
         "value": round(main_r["tflops"], 3),
@@ -426,6 +445,10 @@ def main():
             "traffic_unit": "GB/s (rocprofv3 FETCH_SIZE + WRITE_SIZE bytes per launch / launch time)",
             "traffic_bytes_per_launch": traffic_bytes,
             "launch_ms": round(main_r["attn_ms"], 4),
+            # the spec peak assumes 2.4 GHz; the counter profile gives the clock actually held
+            "profiled_clock_ghz": clock,
+            "frac_at_profiled_clock": None if clock is None else
+            round(main_r["attn_tflops"] / (PEAK_BF16_TFLOPS * clock / 2.4), 4),
         },
         "cpu_baseline": cpu,
         "mask_topk": topk,
