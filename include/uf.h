@@ -147,6 +147,14 @@ typedef struct uf_kvcache_desc {
   float v_scale;
   int32_t block_grid_h;     /* 0, or the frame's token grid (block_grid_h * block_grid_w = L): */
   int32_t block_grid_w;     /* each step is held in (2,8,8) block order (see below) */
+  int32_t max_q_heads;      /* 0, or the most query heads a step will have */
+  int32_t max_q_tokens;     /* 0, or the most queries a step will have; with max_q_heads it caps
+                               uf_attn_workspace_bytes (see there) */
+  int32_t heads_per_wg;     /* 0 = the library's choice; 1, 2 or 4: query heads of one KV group
+                               that share each staged key tile (must divide Hq / n_kv_heads) */
+  int32_t splits;           /* 0 = the library's choice; 1..16: parts of the key range computed
+                               apart and merged (fewer when the workspace or the key tiles do not
+                               allow as many) */
 } uf_kvcache_desc;
 
 /*
@@ -194,8 +202,13 @@ typedef struct uf_append_plan {
 /* Bytes of K storage (same for V) for this description; 0 if it is invalid. */
 size_t uf_kvcache_storage_bytes(const uf_kvcache_desc* desc);
 
-/* Workspace bytes that let every step split its key range as it sees fit
- * (proportional to head_dim, independent of sequence sizes); 0 if invalid. */
+/* Workspace bytes that let every step split its key range as the library
+ * would choose: (head_dim + 2) * 4 bytes per (split, query, head) row, for
+ * at most 256 rows per compute unit of the current device (the library
+ * splits only steps with fewer work items than two per compute unit, so
+ * this never limits its own choice), and at most 16 * max_q_heads *
+ * max_q_tokens rows when both are given.  A forced split count (desc
+ * splits) that would need more is lowered to what fits.  0 if invalid. */
 size_t uf_attn_workspace_bytes(const uf_kvcache_desc* desc);
 
 /* Validate desc and create a handle with no frames appended.  The storage
@@ -210,7 +223,10 @@ uf_status uf_kvcache_destroy(uf_kvcache* cache);
 uf_status uf_kvcache_reset(uf_kvcache* cache);
 
 /* Crop the recent window to its newest active_frames frames, 1..window_frames
- * (Ultra Flash notes, key design 4, item iii).  Takes effect at the next step. */
+ * (Ultra Flash notes, key design 4, item iii).  Takes effect at the next step.
+ * In block order a step's frames share their tiles, so the crop must be a
+ * multiple of the stream's frames per append: UF_ERR_SHAPE here once that
+ * count is known, and from uf_attn_step / uf_block_mask_topk otherwise. */
 uf_status uf_kvcache_set_window(uf_kvcache* cache, int32_t active_frames);
 
 /*

@@ -15,7 +15,8 @@ import oracle
 import oracle.blocks as ob
 import oracle.fp8 as f8
 from synth import WORKLOAD, TILE, Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
-from tests.gpu_util import assert_close, bits_of, f32_of, to_dev
+from tests.fp8_bound import bound as fp8_bound
+from tests.gpu_util import assert_close, bits_of, errors, f32_of, map_row_tiles, oracle_rows, to_dev
 from tests.ring_model import RingModel
 from tests.test_gpu_topk import check_mask
 from windowed_attention_amd import KVCache, uf
@@ -74,12 +75,19 @@ def run_block_stream(cfg, fp8=False, scales=(0.02, 0.015, 0.02)):
         cache.attn_step(to_dev(qb), out, mask_d)
         torch.cuda.synchronize()
         kk, vv = win.keys_values()
-        ref = _unperm(cfg, oracle.attend(_perm(cfg, q), kk, vv, mask_np))
+        qp = _perm(cfg, q)
+        ref_p = oracle.attend(qp, kk, vv, mask_np)
+        ref = _unperm(cfg, ref_p)
         if fp8:
+            # every element within the E4M3 probability bound (tests/fp8_bound.py), which is
+            # evaluated in the oracle's (block) row order and then put back in raster order
             got = f32_of(out).astype(np.float64)
-            err = np.abs(got - ref).max()
-            print(f"  fp8 max_abs={err:.3e}", flush=True)
-            assert err < 0.1
+            bnd = _unperm(cfg, fp8_bound(qp, kk, vv, ref_p, mask_np, np.arange(cfg.q_tokens)))
+            ratio = float((np.abs(got - ref) / bnd).max())
+            ma, rl = errors(got, ref)
+            print(f"  fp8 max_abs={ma:.3e} rel_l2={rl:.3e}, largest error / bound = {ratio:.3f}", flush=True)
+            assert np.isfinite(got).all()
+            assert ratio <= 1.0, f"{cfg.name} step {s}: error beyond the E4M3 probability bound ({ratio:.3f})"
         else:
             assert_close(f32_of(out), ref, f"{cfg.name} step {s}")
     cache.close()
@@ -123,9 +131,11 @@ def test_block_order_topk_mask():
     cache.close()
 
 
+@pytest.mark.timeout(600)
 def test_block_order_2k_sampled():
-    """The 2K chunk held in block order at full size: 4 steps, sampled query tiles of steps 0
-    and 3 (tile t of the block order holds raster tokens order[128 t ...])."""
+    """The 2K chunk held in block order at full size: 4 steps, each compared on 32 seeded query
+    tiles per head (the first, the last and 30 drawn; tile t of the block order holds raster
+    tokens order[128 t ...])."""
     cfg = WORKLOAD["2k"]
     F = cfg.frames_per_step
     order = ob.block_order(F, cfg.grid[0], cfg.grid[1])
@@ -142,13 +152,11 @@ def test_block_order_2k_sampled():
         mask_np = make_block_mask(cfg.index, s, cfg.n_q_heads, cfg.q_tokens, n_k, cfg.mask_pct)
         out = torch.empty_like(to_dev(qb))
         cache.attn_step(to_dev(qb), out, torch.from_numpy(mask_np).to("cuda:0"))
-        if s not in (0, cfg.steps - 1):
-            continue
         torch.cuda.synchronize()
-        tiles = sorted({0, nqt - 1, *np.random.default_rng(s).choice(np.arange(1, nqt - 1), 2, replace=False)})
+        tiles = sorted({0, nqt - 1, *np.random.default_rng(s).choice(np.arange(1, nqt - 1), 30, replace=False)})
         rows = np.concatenate([np.arange(t * TILE, min((t + 1) * TILE, cfg.q_tokens)) for t in tiles])
         kk, vv = win.keys_values()
-        ref = oracle.attend(bf16_bits_to_f32(qb)[order], kk, vv, mask_np, rows=rows)
+        ref = oracle_rows(bf16_bits_to_f32(qb)[order], kk, vv, mask_np, rows)
         got = f32_of(out)[order[rows]]
-        assert_close(got, ref, f"2k block order step {s}, tiles {tiles}")
+        assert_close(got, ref, f"2k block order step {s}, {len(tiles)} tiles")
     cache.close()

@@ -20,7 +20,7 @@ import oracle.fp8 as f8
 from synth import WORKLOAD, TILE, Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
 from tests import fp8_lut
 from tests.fp8_bound import bound as _bound
-from tests.gpu_util import errors, f32_of, to_dev
+from tests.gpu_util import errors, f32_of, map_row_tiles, oracle_rows, to_dev
 from tests.ring_model import RingModel
 from windowed_attention_amd import KVCache, uf
 
@@ -29,10 +29,10 @@ pytestmark = pytest.mark.gpu
 SCALES = (0.02, 0.015, 0.02)  # q, k, v: N(0,1) draws use E4M3's range without saturating
 
 
-def _fp8_cache(cfg, scales=SCALES):
+def _fp8_cache(cfg, scales=SCALES, **kw):
     q_s, k_s, v_s = scales
     return KVCache(cfg.n_kv_heads, cfg.head_dim, cfg.tokens_per_frame, cfg.window_frames, cfg.anchor_frames,
-                   kv_dtype=uf.UF_FP8_E4M3, q_scale=q_s, k_scale=k_s, v_scale=v_s)
+                   kv_dtype=uf.UF_FP8_E4M3, q_scale=q_s, k_scale=k_s, v_scale=v_s, **kw)
 
 
 @pytest.mark.parametrize("case", [(2, 128, 200, 4, 1, 2, 6), (3, 64, 96, 3, 0, 1, 7)],
@@ -77,9 +77,9 @@ def _same_codes(storage, want, what):
     assert len(bad) == 0, f"{what}: {len(bad)} codes differ"
 
 
-def run_fp8_stream(cfg, check_steps=None, tiles=None, scales=SCALES):
+def run_fp8_stream(cfg, check_steps=None, tiles=None, scales=SCALES, **cache_kw):
     q_s, k_s, v_s = scales
-    cache = _fp8_cache(cfg, scales)
+    cache = _fp8_cache(cfg, scales, **cache_kw)
     win = oracle.FrameListWindow(cfg.tokens_per_frame, cfg.window_frames, cfg.anchor_frames)
     check_steps = range(cfg.steps) if check_steps is None else check_steps
     worst = 0.0
@@ -102,12 +102,15 @@ def run_fp8_stream(cfg, check_steps=None, tiles=None, scales=SCALES):
         torch.cuda.synchronize()
         got = f32_of(out)
         nqt = -(-cfg.q_tokens // TILE)
-        sel_tiles = range(nqt) if tiles is None else sorted({0, nqt - 1, *range(1, nqt - 1, max(1, nqt // tiles))})
+        sel_tiles = range(nqt) if tiles is None or tiles >= nqt else \
+            sorted({0, nqt - 1, *np.random.default_rng(s).choice(np.arange(1, nqt - 1), tiles - 2, replace=False)})
         rows = np.concatenate([np.arange(t * TILE, min((t + 1) * TILE, cfg.q_tokens)) for t in sel_tiles])
         qq = fp8_lut.round_trip_bits(qb, q_s)
         kk, vv = win.keys_values()
-        ref = oracle.attend(qq, kk, vv, mask_np, rows=rows)
-        bound = _bound(qq, kk, vv, ref, mask_np, rows)
+        ref = oracle_rows(qq, kk, vv, mask_np, rows)
+        # the bound is row-wise: evaluate it on the same tile groups, each with its rows' ref
+        pos = {int(r): i for i, r in enumerate(rows)}
+        bound = map_row_tiles(lambda r: _bound(qq, kk, vv, ref[[pos[int(x)] for x in r]], mask_np, r), rows)
         err = np.abs(got[rows].astype(np.float64) - ref)
         ratio = float((err / bound).max())
         ma, rl = errors(got[rows], ref)
@@ -132,19 +135,26 @@ def test_fp8_attention_within_bound(cfg):
     run_fp8_stream(cfg)
 
 
-def test_fp8_forced_splits(monkeypatch):
-    monkeypatch.setenv("UF_SPLITS", "3")
-    run_fp8_stream(Workload(64, "f8-split", "bf16", 4, 1, 128, (10, 30), 2, 4, 1, 4, None))
+def test_fp8_forced_splits():
+    run_fp8_stream(Workload(64, "f8-split", "bf16", 4, 1, 128, (10, 30), 2, 4, 1, 4, None), splits=3)
 
 
+@pytest.mark.parametrize("hpw", [2, 4])
+def test_fp8_per_head_masks_shared_tiles(hpw):
+    # per-head masks with a GQA group's heads sharing staged tiles (union walk), GQA 4
+    run_fp8_stream(Workload(66, "f8-union", "bf16", 8, 2, 128, (11, 23), 2, 4, 0, 4, 30), heads_per_wg=hpw)
+
+
+@pytest.mark.timeout(600)
 def test_fp8_1k_shape():
     cfg = Workload(3, "1k", "bf16", 12, 12, 128, (60, 104), 3, 6, 0, 2, 25)
-    run_fp8_stream(cfg, check_steps=[0, 1], tiles=4)
+    run_fp8_stream(cfg, check_steps=[0, 1], tiles=32)
 
 
+@pytest.mark.timeout(600)
 def test_fp8_2k_shape():
-    # the 2K chunk (90x156 tokens per frame, 15% mask) at full size, sampled query tiles
-    run_fp8_stream(WORKLOAD["2k"], check_steps=[0, 3], tiles=3)
+    # the 2K chunk (90x156 tokens per frame, 15% mask) at full size, 32 seeded query tiles per head
+    run_fp8_stream(WORKLOAD["2k"], check_steps=[0, 3], tiles=32)
 
 
 def test_fp8_decoder_shape():

@@ -6,12 +6,13 @@ max-abs <= 2e-2 and relative L2 <= 5e-3 on every compared row.
 
 Full-size workloads (480P, decoder, 1K, 2K, FlashDecoder-XL backbone and
 refinement) stream all their steps in the library's default launch
-configuration; the oracle then checks whole query
-tiles of each checked step (first, last and seeded random tiles), which it
-computes row by row.  Reduced shapes are compared on every row.
+configuration.  At every checked step the oracle computes whole query tiles:
+every tile when a step has at most 32, else 32 seeded tiles (the first, the
+last and 30 drawn without replacement; 4096 rows per head), the same tiles for
+all heads.  One steady 2K step is compared on every row.  480P, 1K and 2K
+check every step; the decoder and the XL shapes check the steps listed in
+their tests.  Reduced shapes are compared on every row of every step.
 """
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -19,7 +20,7 @@ import torch
 import oracle
 from synth import (WORKLOAD, TILE, Workload, bf16_bits_to_f32, draw_normal, draw_step_tensors, f32_to_bf16_bits,
                    make_block_mask)
-from tests.gpu_util import assert_close, bits_of, errors, f32_of, to_dev
+from tests.gpu_util import assert_close, bits_of, errors, f32_of, oracle_rows, to_dev
 from windowed_attention_amd import KVCache, uf
 
 pytestmark = pytest.mark.gpu
@@ -39,13 +40,19 @@ def _pick_tiles(n_q, n_tiles, seed):
     return sorted({0, nqt - 1, *extra.tolist()})
 
 
+SAMPLED_TILES = 32  # query tiles per head compared at a checked step of a full-size workload
+
+
 def run_stream(cfg: Workload, check_steps=None, tiles=None, shared_mask=False, scale_q=1.0, steps=None,
-               raw_fp32_oracle=False):
-    """Stream cfg through the library; compare checked steps against the oracle."""
+               raw_fp32_oracle=False, full_steps=(), **cache_kw):
+    """Stream cfg through the library; compare checked steps against the oracle.
+
+    tiles: query tiles compared per checked step (None = all); steps in full_steps compare
+    every row whatever `tiles` says."""
     L, F, W, A = cfg.tokens_per_frame, cfg.frames_per_step, cfg.window_frames, cfg.anchor_frames
     steps = cfg.steps if steps is None else steps
     check_steps = range(steps) if check_steps is None else check_steps
-    cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, W, A)
+    cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, W, A, **cache_kw)
     win = oracle.FrameListWindow(L, W, A)
     raw = oracle.FrameListWindow(L, W, A) if raw_fp32_oracle else None
     worst = (0.0, 0.0)
@@ -71,14 +78,16 @@ def run_stream(cfg: Workload, check_steps=None, tiles=None, shared_mask=False, s
             continue
         torch.cuda.synchronize()
         got = f32_of(out)
-        rows = _rows_of_tiles(cfg.q_tokens, _pick_tiles(cfg.q_tokens, tiles, 1000 * cfg.index + s))
-        ref = oracle.attend(bf16_bits_to_f32(qb), kk, vv, mask_np, rows=rows)
+        picked = _pick_tiles(cfg.q_tokens, None if s in full_steps else tiles, 1000 * cfg.index + s)
+        rows = _rows_of_tiles(cfg.q_tokens, picked)
+        print(f"  oracle on {len(picked)} query tiles x {cfg.n_q_heads} heads", flush=True)
+        ref = oracle_rows(bf16_bits_to_f32(qb), kk, vv, mask_np, rows)
         ma, rl = assert_close(got[rows], ref, f"{cfg.name} step {s} ({len(rows)} rows)")
         worst = (max(worst[0], ma), max(worst[1], rl))
         if raw is not None:
             rk, rv = raw.keys_values()
             q_raw = draw_normal(cfg.index, s, 0, qb.shape) * np.float32(scale_q)
-            ref_raw = oracle.attend(q_raw, rk, rv, mask_np, rows=rows)
+            ref_raw = oracle_rows(q_raw, rk, rv, mask_np, rows)
             ma_raw, rl_raw = errors(got[rows], ref_raw)
             print(f"  vs float32-input oracle: max_abs={ma_raw:.3e} rel_l2={rl_raw:.3e}", flush=True)
             assert ma_raw < 2e-2 and rl_raw < 1e-2
@@ -94,30 +103,38 @@ def test_tiny_all_steps():
     run_stream(WORKLOAD["tiny"], raw_fp32_oracle=True)
 
 
+@pytest.mark.timeout(600)
 def test_480p_anchor_stream():
-    run_stream(WORKLOAD["480p"], check_steps=[0, 1, 3, 4, 7], tiles=6)
+    run_stream(WORKLOAD["480p"], tiles=SAMPLED_TILES)
 
 
 def test_decoder_gqa_stream():
-    run_stream(WORKLOAD["decoder"], check_steps=[0, 1, 2, 3, 60, 119], tiles=None)
+    # every row of every 8th step (13 query tiles per step) and of the first and last steps
+    run_stream(WORKLOAD["decoder"], check_steps=sorted({0, 1, 2, 3, 119, *range(0, 120, 8)}), tiles=None)
 
 
+@pytest.mark.timeout(600)
 def test_1k_masked_stream():
-    run_stream(WORKLOAD["1k"], tiles=6)
+    run_stream(WORKLOAD["1k"], tiles=SAMPLED_TILES)
 
 
+@pytest.mark.timeout(900)
 def test_2k_masked_stream():
-    run_stream(WORKLOAD["2k"], tiles=5)
+    # 32 tiles per head at steps 0-2; the steady step 3 on every row (330 tiles x 12 heads)
+    run_stream(WORKLOAD["2k"], tiles=SAMPLED_TILES, full_steps=(3,))
 
 
+@pytest.mark.timeout(600)
 def test_decoder_xl_stream():
-    # head_dim 64, 24 query heads over 3 KV heads (8 per group), per-frame steps
-    run_stream(WORKLOAD["decoder-xl"], check_steps=[0, 1, 2, 23], tiles=6)
+    # head_dim 64, 24 query heads over 3 KV heads (8 per group), per-frame steps; 29 query tiles,
+    # so every row of each checked step
+    run_stream(WORKLOAD["decoder-xl"], check_steps=[0, 1, 2, 5, 11, 17, 23], tiles=SAMPLED_TILES)
 
 
+@pytest.mark.timeout(600)
 def test_refine_xl_stream():
-    # temporal refinement: 4-frame steps over an 8-frame window, head_dim 64, GQA 8
-    run_stream(WORKLOAD["refine-xl"], check_steps=[0, 1, 2, 5], tiles=5)
+    # temporal refinement: 4-frame steps over an 8-frame window, head_dim 64, GQA 8; every step
+    run_stream(WORKLOAD["refine-xl"], tiles=SAMPLED_TILES)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -158,17 +175,34 @@ def test_sharp_attention_stress():
     run_stream(cfg, scale_q=4.0)
 
 
-@pytest.mark.parametrize("splits", ["1", "3", "7"])
-def test_forced_splits(splits, monkeypatch):
-    monkeypatch.setenv("UF_SPLITS", splits)
-    run_stream(Workload(17, "r-split", "bf16", 4, 1, 128, (10, 30), 2, 4, 1, 5, None))
-    run_stream(Workload(18, "r-split-mask", "bf16", 2, 2, 64, (10, 30), 2, 4, 0, 4, 30))
+@pytest.mark.parametrize("splits", [1, 3, 7])
+def test_forced_splits(splits):
+    run_stream(Workload(17, "r-split", "bf16", 4, 1, 128, (10, 30), 2, 4, 1, 5, None), splits=splits)
+    run_stream(Workload(18, "r-split-mask", "bf16", 2, 2, 64, (10, 30), 2, 4, 0, 4, 30), splits=splits)
 
 
-@pytest.mark.parametrize("hpw", ["1", "2", "4"])
-def test_heads_per_workgroup(hpw, monkeypatch):
-    monkeypatch.setenv("UF_HEADS_PER_WG", hpw)
-    run_stream(Workload(19, "r-hpw", "bf16", 8, 2, 128, (10, 25), 1, 3, 0, 3, None))
+@pytest.mark.parametrize("hpw", [1, 2, 4])
+def test_heads_per_workgroup(hpw):
+    run_stream(Workload(19, "r-hpw", "bf16", 8, 2, 128, (10, 25), 1, 3, 0, 3, None), heads_per_wg=hpw)
+
+
+@pytest.mark.parametrize("hpw", [2, 4])
+def test_per_head_masks_shared_tiles(hpw):
+    """Per-head masks with the heads of a KV group sharing staged tiles (the work-group walks the
+    union of its heads' mask rows; each wave computes only its own head's kept tiles): GQA 4
+    (head_dim 128, anchor, ragged) and GQA 8 (head_dim 64, forced splits)."""
+    run_stream(Workload(36, "r-union4", "bf16", 8, 2, 128, (11, 23), 2, 4, 2, 5, 30), heads_per_wg=hpw)
+    run_stream(Workload(37, "r-union8", "bf16", 16, 2, 64, (9, 29), 1, 3, 0, 4, 25), heads_per_wg=hpw,
+               splits=3)
+
+
+def test_per_head_masks_shared_tiles_decoder_xl():
+    """The FlashDecoder-XL backbone shape (24 query heads over 3 KV heads, head_dim 64) under
+    seeded per-head masks of 40% density, four query heads per work-group."""
+    cfg = WORKLOAD["decoder-xl"]
+    cfg = Workload(38, "decoder-xl-masked", cfg.dtype, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.grid,
+                   cfg.frames_per_step, cfg.window_frames, cfg.anchor_frames, 4, 40)
+    run_stream(cfg, heads_per_wg=4)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -253,20 +287,16 @@ def test_no_queries_is_a_no_op():
 def test_splits_agree():
     """Split-KV partials combine to the unsplit result within fp32 rounding (bf16 output: 1 ulp)."""
     cfg = Workload(32, "split-agree", "bf16", 4, 2, 128, (20, 30), 1, 3, 0, 3, None)
-    cache = KVCache(2, 128, 600, 3, 0)
-    for s in range(3):
-        qb, kb, vb = draw_step_tensors(cfg, s)
-        cache.append(to_dev(kb), to_dev(vb), 1)
-    q = to_dev(qb)
     outs = []
-    for splits in ("1", "2", "5"):
-        os.environ["UF_SPLITS"] = splits
-        try:
-            o = torch.empty_like(q)
-            cache.attn_step(q, o)
-            outs.append(f32_of(o))
-        finally:
-            del os.environ["UF_SPLITS"]
+    for splits in (1, 2, 5):
+        cache = KVCache(2, 128, 600, 3, 0, splits=splits)
+        for s in range(3):
+            qb, kb, vb = draw_step_tensors(cfg, s)
+            cache.append(to_dev(kb), to_dev(vb), 1)
+        q = to_dev(qb)
+        o = torch.empty_like(q)
+        cache.attn_step(q, o)
+        outs.append(f32_of(o))
+        cache.close()
     for o in outs[1:]:
         assert np.abs(o - outs[0]).max() <= 2.0 ** -7 * np.abs(outs[0]).max() + 1e-6
-    cache.close()

@@ -45,8 +45,11 @@ def test_status_strings():
     assert uf.uf_status_string(-5) == "UF_ERR_STATE"
 
 
-def desc(H=2, d=128, L=64, W=3, A=0, k=KS, v=VS, ws=None, ws_bytes=0):
-    return uf.uf_kvcache_desc(H, d, L, W, A, k, v, ws, ws_bytes)
+def desc(H=2, d=128, L=64, W=3, A=0, k=KS, v=VS, ws=None, ws_bytes=0, hpw=0, splits=0, max_q_heads=0,
+         max_q_tokens=0):
+    dd = uf.uf_kvcache_desc(H, d, L, W, A, k, v, ws, ws_bytes)
+    dd.heads_per_wg, dd.splits, dd.max_q_heads, dd.max_q_tokens = hpw, splits, max_q_heads, max_q_tokens
+    return dd
 
 
 def create(**kw):
@@ -67,6 +70,12 @@ def create(**kw):
     (dict(ws_bytes=1024), uf.UF_ERR_INVALID_ARG),          # size without a pointer
     (dict(ws=FAKE * 8 + 16, ws_bytes=1024), uf.UF_ERR_INVALID_ARG),  # misaligned workspace
     (dict(L=1 << 20, W=4096), uf.UF_ERR_CAPACITY),
+    (dict(hpw=3), uf.UF_ERR_INVALID_ARG),
+    (dict(hpw=8), uf.UF_ERR_INVALID_ARG),
+    (dict(splits=17), uf.UF_ERR_INVALID_ARG),
+    (dict(splits=-1), uf.UF_ERR_INVALID_ARG),
+    (dict(max_q_heads=-1), uf.UF_ERR_INVALID_ARG),
+    (dict(max_q_tokens=-5), uf.UF_ERR_INVALID_ARG),
 ])
 def test_create_rejects(kw, status):
     st, h = create(**kw)
@@ -80,7 +89,13 @@ def test_sizes():
     assert uf.uf_kvcache_storage_bytes(d) == 3 * 2 * 1560 * 128 * 2
     d = desc(H=12, d=128, L=1560, W=9, A=3)
     assert uf.uf_kvcache_storage_bytes(d) == 12 * 12 * 1560 * 128 * 2
-    assert uf.uf_attn_workspace_bytes(d) > 0
+    # without a GPU the library assumes 256 compute units: 2 * 256 * 128 (split, query, head) rows
+    full = uf.uf_attn_workspace_bytes(d)
+    assert full == 2 * 256 * 128 * (128 + 2) * 4
+    # with the step's largest size given, at most 16 splits of it
+    assert uf.uf_attn_workspace_bytes(desc(H=3, d=64, L=1560, W=2, max_q_heads=12, max_q_tokens=100)) == \
+        16 * 12 * 100 * (64 + 2) * 4
+    assert uf.uf_attn_workspace_bytes(desc(H=12, d=128, L=1560, W=9, A=3, max_q_heads=12, max_q_tokens=4680)) == full
     assert uf.uf_kvcache_storage_bytes(desc(d=80)) == 0
 
 
@@ -352,3 +367,86 @@ def test_block_order_validation():
         assert LIB.uf_kvcache_append(h, None, None, 1, uf.UF_APPEND_COMMIT_ONLY, None) == uf.UF_OK  # new stream
     finally:
         uf.uf_kvcache_destroy(h)
+
+
+def test_block_order_crop_keeps_whole_steps():
+    """In block order every frame slot of a step holds tokens of all the step's frames, so a
+    crop of the recent window must be a whole number of steps."""
+    d = desc(H=2, d=128, L=200, W=4, A=0)
+    d.block_grid_h, d.block_grid_w = 10, 20
+    h = ctypes.c_void_p()
+    assert LIB.uf_kvcache_create(ctypes.byref(d), ctypes.byref(h)) == uf.UF_OK
+    h = h.value
+    q, out = _tensor(400, 4, data=FAKE * 32), _tensor(400, 4, data=FAKE * 64)
+    p = uf.uf_topk_params(1, 0)
+    try:
+        # before the first append the step size is unknown: the crop is accepted here, and the
+        # step that would use it refuses
+        assert LIB.uf_kvcache_set_window(h, 3) == uf.UF_OK
+        for _ in range(3):
+            assert LIB.uf_kvcache_append(h, None, None, 2, uf.UF_APPEND_COMMIT_ONLY, None) == uf.UF_OK
+        assert LIB.uf_attn_step(ctypes.byref(q), h, None, ctypes.byref(out), None) == uf.UF_ERR_SHAPE
+        assert "multiple" in uf.uf_last_error()
+        assert LIB.uf_block_mask_topk(ctypes.byref(q), h, ctypes.byref(p), FAKE * 512, None, FAKE * 256, 1 << 30,
+                                      None) == uf.UF_ERR_SHAPE
+        # once the step size is known the crop itself is refused and the window stays as it was
+        assert LIB.uf_kvcache_set_window(h, 2) == uf.UF_OK
+        before = _window(h)
+        assert LIB.uf_kvcache_set_window(h, 1) == uf.UF_ERR_SHAPE
+        assert LIB.uf_kvcache_set_window(h, 3) == uf.UF_ERR_SHAPE
+        assert _window(h) == before
+        assert before["n_keys"] == 2 * 200
+        assert LIB.uf_kvcache_set_window(h, 4) == uf.UF_OK
+    finally:
+        uf.uf_kvcache_destroy(h)
+
+
+def test_heads_per_wg_must_divide_the_group():
+    st, h = create(H=2, d=128, L=100, W=3, hpw=4)
+    assert st == uf.UF_OK
+    try:
+        uf.uf_kvcache_append(h, None, None, 2, uf.UF_APPEND_COMMIT_ONLY, 0)
+        q, out = _tensor(200, 4, data=FAKE * 32), _tensor(200, 4, data=FAKE * 64)   # 2 query heads per KV head
+        assert LIB.uf_attn_step(ctypes.byref(q), h, None, ctypes.byref(out), None) == uf.UF_ERR_SHAPE
+        assert "heads_per_wg" in uf.uf_last_error()
+    finally:
+        uf.uf_kvcache_destroy(h)
+
+
+def _stub_launches():
+    try:
+        return LIB.uf_stub_launch_count()
+    except AttributeError:
+        return None
+
+
+@pytest.mark.skipif(_stub_launches() is None, reason="only with the host-only build (launch stubs)")
+def test_valid_calls_reach_the_launchers():
+    """With the host-only build every valid call runs its whole host path (window bookkeeping,
+    launch parameters) and reaches the launchers, which check their invariants; each call
+    launches what its contract says: append 1, step 1 (2 when split), mask generation 1."""
+    ws_bytes = uf.uf_attn_workspace_bytes(desc(H=2, d=128, L=200, W=4, A=1))
+    for hpw, splits in ((0, 0), (1, 3), (2, 2), (0, 16)):
+        st, h = create(H=2, d=128, L=200, W=4, A=1, ws=FAKE * 1024, ws_bytes=ws_bytes, hpw=hpw, splits=splits)
+        assert st == uf.UF_OK, uf.uf_last_error()
+        try:
+            q, out = _tensor(400, 4, data=FAKE * 32), _tensor(400, 4, data=FAKE * 64)
+            for step in range(7):
+                n0 = _stub_launches()
+                k, v = _tensor(400, 2, data=FAKE * 96), _tensor(400, 2, data=FAKE * 128)
+                assert LIB.uf_kvcache_append(h, ctypes.byref(k), ctypes.byref(v), 2, 0, None) == uf.UF_OK
+                assert _stub_launches() == n0 + 1
+                nkt = -(-_window(h)["n_keys"] // 128)
+                m = _mask(4, 4, nkt)
+                got = LIB.uf_attn_step(ctypes.byref(q), h, ctypes.byref(m) if step % 2 else None,
+                                       ctypes.byref(out), None)
+                assert got == uf.UF_OK, uf.uf_last_error()
+                assert _stub_launches() in (n0 + 2, n0 + 3)
+                if splits > 1:
+                    assert _stub_launches() == n0 + 3
+                need = uf.uf_block_mask_workspace_bytes(desc(H=2, d=128, L=200, W=4, A=1), 400, 4)
+                got = LIB.uf_block_mask_topk(ctypes.byref(q), h, ctypes.byref(uf.uf_topk_params(2, 1)), FAKE * 512,
+                                             None, FAKE * 256, need, None)
+                assert got == uf.UF_OK, uf.uf_last_error()
+        finally:
+            uf.uf_kvcache_destroy(h)

@@ -143,6 +143,31 @@ def check_against_sdpa():
         assert err < 1e-12, (c, err)
 
 
+def check_row_subset_matches_sdpa():
+    """attend(rows=r) gives row r of SDPA's full output for any subset r: unsorted, repeated,
+    spanning several query tiles with their own per-head mask rows, ragged last tiles."""
+    cases = [
+        dict(seed=80, n_q=300, n_k=520, hq=6, hkv=3, d=64, mask_heads=6),     # per-head mask, GQA 2
+        dict(seed=90, n_q=333, n_k=290, hq=4, hkv=1, d=32, mask_heads=1),     # shared mask, GQA 4
+        dict(seed=95, n_q=210, n_k=400, hq=2, hkv=2, d=64),                   # dense
+    ]
+    for c in cases:
+        _, ref = _sdpa_case(**c)
+        rng = np.random.default_rng(c["seed"])
+        rows = np.concatenate([rng.choice(c["n_q"], size=40, replace=False), [c["n_q"] - 1, 0, 0, 129, 128, 127]])
+        q = _bf16_normal(c["seed"], (c["n_q"], c["hq"], c["d"]))
+        k = _bf16_normal(c["seed"] + 1, (c["n_k"], c["hkv"], c["d"]))
+        v = _bf16_normal(c["seed"] + 2, (c["n_k"], c["hkv"], c["d"]))
+        bm = None
+        if c.get("mask_heads") is not None:
+            bm = (np.random.default_rng(c["seed"]).random((c["mask_heads"], -(-c["n_q"] // 128),
+                                                            -(-c["n_k"] // 128))) < 0.4).astype(np.uint8)
+            bm[..., 0] = 1
+        sub = oracle.attend(q, k, v, bm, rows=rows)
+        assert sub.shape == (len(rows), c["hq"], c["d"])
+        assert np.abs(sub - ref[rows]).max() < 1e-12, c
+
+
 def check_empty_row_is_zero():
     q = _bf16_normal(70, (256, 2, 64))
     k = _bf16_normal(71, (256, 2, 64))
@@ -268,7 +293,8 @@ def check_executed_pairs():
 
 ALL_CHECKS = [
     check_two_key_worked_example, check_single_key_returns_value, check_identical_keys_give_mean_value,
-    check_window_tables, check_uniform_queries_reveal_window, check_against_sdpa, check_empty_row_is_zero,
+    check_window_tables, check_uniform_queries_reveal_window, check_against_sdpa, check_row_subset_matches_sdpa,
+    check_empty_row_is_zero,
     check_gqa_equals_repeated_mha, check_key_permutation_invariance, check_all_ones_mask_equals_dense,
     check_mask_equals_gathered_dense, check_single_tile_uniform_query, check_streaming_equals_full_sequence,
     check_overwrite_and_crop, check_executed_pairs,
@@ -323,6 +349,32 @@ MUTANTS = {
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(monkeypatch, name):
     assert _caught(monkeypatch, MUTANTS[name]) > 0
+
+
+_ORIG_ATTEND = oracle.attend
+
+
+def _attend_rows_sorted(q, k, v, block_mask=None, rows=None, tile=128):
+    out = _ORIG_ATTEND(q, k, v, block_mask, None, tile)
+    return out if rows is None else out[np.sort(np.asarray(rows))]
+
+
+def _attend_rows_tile_by_position(q, k, v, block_mask=None, rows=None, tile=128):
+    # takes each returned row's mask row from its position in `rows`, not from the row itself
+    if rows is None:
+        return _ORIG_ATTEND(q, k, v, block_mask, None, tile)
+    rows = np.asarray(rows)
+    out = np.stack([_ORIG_ATTEND(q[[r]], k, v, None if block_mask is None else
+                                 block_mask[:, [min(i // tile, block_mask.shape[1] - 1)]], None, tile)[0]
+                    for i, r in enumerate(rows)])
+    return out
+
+
+@pytest.mark.parametrize("mutant", [_attend_rows_sorted, _attend_rows_tile_by_position], ids=lambda f: f.__name__)
+def test_row_subset_mutant_is_caught(monkeypatch, mutant):
+    monkeypatch.setattr(oracle, "attend", mutant)
+    with pytest.raises(AssertionError):
+        check_row_subset_matches_sdpa()
 
 
 def test_scale_mutant_is_caught(monkeypatch):

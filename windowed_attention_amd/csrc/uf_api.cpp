@@ -40,9 +40,6 @@ uf_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;
-// Split partials are budgeted in (query, head) rows: at most this many rows
-// times splits, which bounds the workspace independently of the step size.
-constexpr int64_t kSplitRowBudget = 1024 * 128;
 constexpr int kMaxSplits = 16;
 
 uf_status check_desc(const uf_kvcache_desc* d) {
@@ -60,6 +57,12 @@ uf_status check_desc(const uf_kvcache_desc* d) {
       (d->block_grid_h && (int64_t)d->block_grid_h * d->block_grid_w != d->tokens_per_frame))
     return fail(UF_ERR_SHAPE, "block grid %d x %d does not give %d tokens per frame", d->block_grid_h,
                 d->block_grid_w, d->tokens_per_frame);
+  if (d->max_q_heads < 0 || d->max_q_tokens < 0)
+    return fail(UF_ERR_INVALID_ARG, "max_q_heads and max_q_tokens must be >= 0");
+  if (d->heads_per_wg != 0 && d->heads_per_wg != 1 && d->heads_per_wg != 2 && d->heads_per_wg != 4)
+    return fail(UF_ERR_INVALID_ARG, "heads_per_wg must be 0, 1, 2 or 4 (got %d)", d->heads_per_wg);
+  if (d->splits < 0 || d->splits > kMaxSplits)
+    return fail(UF_ERR_INVALID_ARG, "splits must lie in 0..%d (got %d)", kMaxSplits, d->splits);
   if (d->kv_dtype != UF_BF16 && d->kv_dtype != UF_FP8_E4M3)
     return fail(UF_ERR_DTYPE, "kv_dtype must be UF_BF16 or UF_FP8_E4M3 (got %d)", d->kv_dtype);
   if (d->kv_dtype == UF_FP8_E4M3) {
@@ -174,6 +177,25 @@ int device_cu_count() {
   return cached_cus;
 }
 
+// Split partials are budgeted in (split, query, head) rows.  The library splits a step only
+// when it has fewer work items (128 rows each) than two per compute unit, and then into at
+// most 2 * CUs / items parts, so it never needs more than 2 * CUs * 128 rows.
+int64_t split_row_budget(const uf_kvcache_desc& d) {
+  int64_t rows = 2 * (int64_t)device_cu_count() * UF_TILE;
+  if (d.max_q_heads > 0 && d.max_q_tokens > 0)
+    rows = std::min<int64_t>(rows, (int64_t)kMaxSplits * d.max_q_heads * d.max_q_tokens);
+  return rows;
+}
+
+// The crop of a block-order stream must keep whole steps: every frame slot of a step holds
+// tokens of all the step's frames.
+uf_status check_block_crop(const uf_kvcache* c) {
+  if (c->d.block_grid_h && c->block_frames && c->active % c->block_frames)
+    return fail(UF_ERR_SHAPE, "block order: the window crop (%d frames) must be a multiple of the %d frames per step",
+                c->active, c->block_frames);
+  return UF_OK;
+}
+
 // Bytes of the query-tile means in the mask-generation workspace, rounded up
 // so that the key-tile means after them start 256-byte aligned.
 size_t topk_workspace_split(int64_t q_tiles_times_heads, int head_dim) {
@@ -192,7 +214,7 @@ size_t uf_kvcache_storage_bytes(const uf_kvcache_desc* desc) {
 
 size_t uf_attn_workspace_bytes(const uf_kvcache_desc* desc) {
   if (!desc || check_desc(desc) != UF_OK) return 0;
-  return (size_t)kSplitRowBudget * (desc->head_dim + 2) * sizeof(float);
+  return (size_t)split_row_budget(*desc) * (desc->head_dim + 2) * sizeof(float);
 }
 
 uf_status uf_kvcache_create(const uf_kvcache_desc* desc, uf_kvcache** out) {
@@ -237,8 +259,11 @@ uf_status uf_kvcache_set_window(uf_kvcache* cache, int32_t active_frames) {
   if (!cache) return fail(UF_ERR_INVALID_ARG, "cache is NULL");
   if (active_frames < 1 || active_frames > cache->d.window_frames)
     return fail(UF_ERR_SHAPE, "active_frames must lie in 1..%d (got %d)", cache->d.window_frames, active_frames);
+  const int32_t before = cache->active;
   cache->active = active_frames;
-  return UF_OK;
+  const uf_status s = check_block_crop(cache);
+  if (s != UF_OK) cache->active = before;
+  return s;
 }
 
 uf_status uf_kvcache_window(const uf_kvcache* cache, uf_window_info* out) {
@@ -346,6 +371,7 @@ uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mas
   if (d.block_grid_h && n_q != 0 && (int64_t)n_q != (int64_t)cache->block_frames * d.tokens_per_frame)
     return fail(UF_ERR_SHAPE, "block order: the queries must be the step's %lld tokens (got %d)",
                 (long long)cache->block_frames * d.tokens_per_frame, n_q);
+  if ((s = check_block_crop(cache)) != UF_OK) return s;
   const int n_qt = (n_q + UF_TILE - 1) / UF_TILE;
   const int n_kt = (w.n_keys + UF_TILE - 1) / UF_TILE;
   if (mask) {
@@ -362,11 +388,17 @@ uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mas
 
   const int group = hq / d.n_kv_heads;
   const bool per_head_mask = mask && mask->n_heads > 1;
+  // Query heads of one KV group per work-group.  With a dense or shared mask every head of the
+  // work-group keeps the same tiles, so sharing each staged tile is free.  With per-head masks
+  // the work-group walks the union of its heads' rows and a wave skips the tiles its own head
+  // does not keep; that pays only when the heads' rows overlap, so it is taken on request.
   int hpw = 1;
-  if (!per_head_mask) hpw = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
-  if (const char* e = getenv("UF_HEADS_PER_WG")) {
-    const int v = atoi(e);
-    if ((v == 1 || v == 2 || v == 4) && group % v == 0 && (v == 1 || !per_head_mask)) hpw = v;
+  if (d.heads_per_wg) {
+    hpw = d.heads_per_wg;
+    if (group % hpw)
+      return fail(UF_ERR_SHAPE, "heads_per_wg %d does not divide the %d query heads per KV head", hpw, group);
+  } else if (!per_head_mask) {
+    hpw = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
   }
   const int qpw = UF_TILE / hpw;
   const int n_qblk = (n_q + qpw - 1) / qpw;
@@ -383,10 +415,7 @@ uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mas
     splits = (int)std::min<int64_t>(std::max<int64_t>(1, (2 * cus) / items), kMaxSplits);
     splits = std::min(splits, std::max(1, n_kt / 4));
   }
-  if (const char* e = getenv("UF_SPLITS")) {
-    const int v = atoi(e);
-    if (v >= 1 && v <= kMaxSplits) splits = std::min(v, n_kt);
-  }
+  if (d.splits) splits = std::min(d.splits, n_kt);
   const int64_t rows = (int64_t)n_q * hq;
   const auto fits = [&](int s) {
     return s == 1 || (int64_t)s * rows * (d.head_dim + 2) * (int64_t)sizeof(float) <= (int64_t)d.workspace_bytes;
@@ -480,6 +509,7 @@ uf_status uf_block_mask_topk(const uf_tensor* q, const uf_kvcache* cache, const 
   const int32_t n_q = q->n_tokens, hq = q->n_heads;
   if (n_q > w.n_keys)
     return fail(UF_ERR_SHAPE, "%d queries but only %d visible keys: queries must be the newest keys", n_q, w.n_keys);
+  if ((s = check_block_crop(cache)) != UF_OK) return s;
   if (d.block_grid_h && n_q != 0 && (int64_t)n_q != (int64_t)cache->block_frames * d.tokens_per_frame)
     return fail(UF_ERR_SHAPE, "block order: the queries must be the step's %lld tokens (got %d)",
                 (long long)cache->block_frames * d.tokens_per_frame, n_q);

@@ -324,16 +324,18 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
   // Tile i sits in buffer i % 2.  The barrier at the top of step i publishes tile i (every
   // wave has waited for its own copies) and also shows that every wave has finished tile
   // i - 1, whose buffer the copy of tile i + 1 then overwrites.
-  int kt = tiles.next(lane);
+  bool own, own_next;
+  int kt = tiles.next(lane, own);
   int buf = 0;
   if (kt >= 0) issue(kt, 0);
   while (kt >= 0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int kn = tiles.next(lane);
+    const int kn = tiles.next(lane, own_next);
     if (kn >= 0) issue(kn, buf ^ 1);
-    compute(min(kTile, p.n_k - kt * kTile), buf);
+    if (own) compute(min(kTile, p.n_k - kt * kTile), buf);
     kt = kn;
+    own = own_next;
     buf ^= 1;
   }
 

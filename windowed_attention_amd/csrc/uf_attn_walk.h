@@ -62,42 +62,62 @@ __device__ inline int contiguous_tile_rows(const AttnParams& p, int kt) {
 
 // The kept key tiles of one work item's mask row (every tile of its key range without a
 // mask), in ascending order: 64 tiles at a time from a wave ballot over the mask row.  The
-// tile returned is the same on every lane of the wave (and every wave of the work-group:
-// heads_per_wg > 1 only with a mask shared by all heads).
+// tile returned is the same on every lane of the wave and every wave of the work-group.  With
+// per-head masks and heads_per_wg > 1 the walk covers the union of the work-group's heads'
+// rows, and `own` says whether the calling wave's head keeps the tile (its waves skip the
+// others); otherwise `own` is always true.
 struct KeyTiles {
-  const uint8_t* mrow;
+  const uint8_t* mrow;     // first mask row of the walk (null: dense)
+  const uint8_t* own_row;  // this wave's head's row
+  int64_t row_stride;      // between the heads' rows of a union walk
+  int n_rows;              // rows in the union (1 unless per-head masks are shared by the work-group)
   int hi, w0;
-  uint64_t bits;
+  uint64_t bits, own_bits;
 
   __device__ KeyTiles(const AttnParams& p, const AttnItem& it) {
     const int nkt = (p.n_k + kAttnTile - 1) / kAttnTile;
     const int lo = (int)(((int64_t)it.split * nkt) / p.splits);
     hi = (int)(((int64_t)(it.split + 1) * nkt) / p.splits);
     w0 = lo - 64;
-    bits = 0;
-    mrow = nullptr;
+    bits = own_bits = 0;
+    mrow = own_row = nullptr;
+    row_stride = 0;
+    n_rows = 1;
     if (p.mask) {
-      const int mh = p.mask_heads == 1 ? 0 : it.head;
-      mrow = p.mask + mh * p.mask_stride_head + (int64_t)it.q_tile * p.mask_stride_q;
+      const int64_t qoff = (int64_t)it.q_tile * p.mask_stride_q;
+      if (p.mask_heads == 1) {
+        mrow = own_row = p.mask + qoff;
+      } else {
+        const int h0 = it.head - it.head % p.heads_per_wg;  // the work-group's first head
+        mrow = p.mask + h0 * p.mask_stride_head + qoff;
+        own_row = p.mask + it.head * p.mask_stride_head + qoff;
+        row_stride = p.mask_stride_head;
+        n_rows = p.heads_per_wg;
+      }
     }
   }
 
   // next kept tile, or -1 when the row is exhausted
-  __device__ int next(int lane) {
+  __device__ int next(int lane, bool& own) {
     while (bits == 0) {
       w0 += 64;
       if (w0 >= hi) return -1;
       if (mrow) {
         const int kt = w0 + lane;
-        bits = __ballot(kt < hi && mrow[kt] != 0);
+        bool any = false;
+        if (kt < hi)
+          for (int r = 0; r < n_rows; ++r) any |= mrow[r * row_stride + kt] != 0;
+        bits = __ballot(any);
+        own_bits = n_rows == 1 ? bits : __ballot(kt < hi && own_row[kt] != 0);
       } else {
         const int n = min(64, hi - w0);
-        bits = n == 64 ? ~0ull : ((1ull << n) - 1ull);
+        bits = own_bits = n == 64 ? ~0ull : ((1ull << n) - 1ull);
       }
     }
-    const int kt = w0 + __builtin_ctzll(bits);
+    const int b = __builtin_ctzll(bits);
     bits &= bits - 1;
-    return __builtin_amdgcn_readfirstlane(kt);
+    own = __builtin_amdgcn_readfirstlane((int)((own_bits >> b) & 1)) != 0;
+    return __builtin_amdgcn_readfirstlane(w0 + b);
   }
 };
 

@@ -269,11 +269,12 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
   };
 
   // ---- main loop: the other work-group on this CU computes while this one loads
-  for (int kt = tiles.next(lane); kt >= 0; kt = tiles.next(lane)) {
+  bool own;
+  for (int kt = tiles.next(lane, own); kt >= 0; kt = tiles.next(lane, own)) {
     issue(kt);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // the tile is in LDS for every wave
-    compute(min(kTile, p.n_k - kt * kTile));
+    if (own) compute(min(kTile, p.n_k - kt * kTile));
     __syncthreads();  // every wave is done with the tile before the next one lands
   }
 

@@ -12,7 +12,9 @@ import ctypes
 import os
 from typing import Optional
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libuf.so")
+# UF_LIBRARY_PATH names another build of the same C ABI to load instead (the tests use it for
+# a host-only build of the host side under sanitizers).
+_LIB_PATH = os.environ.get("UF_LIBRARY_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libuf.so")
 
 UF_OK = 0
 UF_ERR_INVALID_ARG = -1
@@ -50,7 +52,9 @@ class uf_kvcache_desc(ctypes.Structure):
                 ("v_storage", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("kv_dtype", ctypes.c_int32),
                 ("q_scale", ctypes.c_float), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
-                ("block_grid_h", ctypes.c_int32), ("block_grid_w", ctypes.c_int32)]
+                ("block_grid_h", ctypes.c_int32), ("block_grid_w", ctypes.c_int32),
+                ("max_q_heads", ctypes.c_int32), ("max_q_tokens", ctypes.c_int32),
+                ("heads_per_wg", ctypes.c_int32), ("splits", ctypes.c_int32)]
 
 
 class uf_block_mask(ctypes.Structure):
@@ -246,18 +250,27 @@ class KVCache:
 
     def __init__(self, n_kv_heads: int, head_dim: int, tokens_per_frame: int, window_frames: int,
                  anchor_frames: int = 0, device="cuda", workspace: bool = True, kv_dtype: int = UF_BF16,
-                 q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0, block_grid=(0, 0)):
+                 q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0, block_grid=(0, 0),
+                 max_q_heads: int = 0, max_q_tokens: int = 0, heads_per_wg: int = 0, splits: int = 0,
+                 k_storage=None, v_storage=None):
+        """k_storage / v_storage: caller-made device tensors of the storage's shape
+        [n_kv_heads, (anchor_frames + window_frames) * tokens_per_frame, head_dim] (bf16, or uint8
+        for FP8), e.g. views into larger buffers; allocated here when not given."""
         import torch
         desc = uf_kvcache_desc(n_kv_heads, head_dim, tokens_per_frame, window_frames, anchor_frames,
                                None, None, None, 0, kv_dtype, q_scale, k_scale, v_scale,
-                               block_grid[0], block_grid[1])
+                               block_grid[0], block_grid[1], max_q_heads, max_q_tokens, heads_per_wg, splits)
         nbytes = uf_kvcache_storage_bytes(desc)
         if nbytes == 0:
             _check(_lib.uf_kvcache_create(ctypes.byref(desc), ctypes.byref(ctypes.c_void_p())), "KVCache")
         rows = (anchor_frames + window_frames) * tokens_per_frame
         tdt = torch.uint8 if kv_dtype == UF_FP8_E4M3 else torch.bfloat16
-        self.k_storage = torch.empty((n_kv_heads, rows, head_dim), dtype=tdt, device=device)
-        self.v_storage = torch.empty_like(self.k_storage)
+        shape = (n_kv_heads, rows, head_dim)
+        for t in (k_storage, v_storage):
+            if t is not None and (tuple(t.shape) != shape or t.dtype != tdt or not t.is_contiguous()):
+                raise ValueError(f"storage must be a contiguous {tdt} tensor of shape {shape}")
+        self.k_storage = torch.empty(shape, dtype=tdt, device=device) if k_storage is None else k_storage
+        self.v_storage = torch.empty_like(self.k_storage) if v_storage is None else v_storage
         ws_bytes = uf_attn_workspace_bytes(desc) if workspace else 0
         self.workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
         desc.k_storage = self.k_storage.data_ptr()
