@@ -265,6 +265,26 @@ uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mas
                        uf_tensor* out, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): uf_attn_step with the same arguments, results and
+ * errors, except that split partials go to scratch memory the library holds itself (a
+ * file-scope device array of UF_STATIC_SCRATCH_BYTES on each GPU it runs on, kept until the
+ * process ends) instead of the cache's workspace, which may then be absent.  Neither this
+ * call nor its first use on a device allocates (no hipMalloc, no allocating library routine);
+ * its first call on a device looks up the array's device address once.  The split count is
+ * chosen as uf_attn_step chooses it with a workspace of UF_STATIC_SCRATCH_BYTES; a split
+ * count forced through the cache description (desc splits) whose partials,
+ * splits * Nq * Hq * (head_dim + 2) * 4 bytes, exceed UF_STATIC_SCRATCH_BYTES is refused
+ * with UF_ERR_CAPACITY.  Every partial is written before it is read, so nothing needs
+ * clearing between calls.  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU (other streams, other threads, other caches) race and must be
+ * ordered by the caller.
+ */
+#define UF_STATIC_SCRATCH_BYTES (32u << 20)
+uf_status uf_attn_step_static(const uf_tensor* q, uf_kvcache* cache, const uf_block_mask* block_mask,
+                              uf_tensor* out, void* stream);
+
+/*
  * Block-mask generation (Ultra Flash notes, key design 3, dynamic
  * block-sparse causal attention): each head rates every (query tile, key
  * tile) pair by the dot product of the two tiles' mean-pooled q and k, and

@@ -2,6 +2,7 @@
 // (uf_api.cpp) without GPU code, e.g. under AddressSanitizer and UndefinedBehaviorSanitizer.
 // Each launcher checks the invariants the real kernels rely on for their parameters, counts
 // the call and launches nothing.
+#include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -21,6 +22,12 @@ void require(bool ok, const char* what) {
 extern "C" int uf_stub_launch_count(void) { return g_launches; }
 
 namespace uf {
+
+// stands in for the device array's address: never dereferenced by the stubs
+hipError_t static_scratch(void** ptr) {
+  *ptr = reinterpret_cast<void*>((uintptr_t)1 << 44);
+  return hipSuccess;
+}
 
 hipError_t launch_append(const AppendParams& p, hipStream_t) {
   require(p.n_tok > 0 && p.n_heads > 0 && (p.head_dim == 64 || p.head_dim == 128), "append sizes");

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     assert sorted(uf.EXPORTED) == names
     out = subprocess.run(["nm", "-D", "--defined-only", uf._LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (uf_\w+)$", out, flags=re.M))
@@ -450,3 +450,41 @@ def test_valid_calls_reach_the_launchers():
                 assert got == uf.UF_OK, uf.uf_last_error()
         finally:
             uf.uf_kvcache_destroy(h)
+
+
+def test_static_step_validates_like_the_step():
+    """uf_attn_step_static checks its arguments as uf_attn_step does, before any HIP call, and
+    refuses a forced split count whose partials exceed its scratch."""
+    st, h = create(H=1, d=128, L=4100, W=2, splits=16)
+    assert st == uf.UF_OK
+    q, out = _tensor(4100, 16, data=FAKE * 32), _tensor(4100, 16, data=FAKE * 64)
+    try:
+        assert LIB.uf_attn_step_static(ctypes.byref(q), h, None, ctypes.byref(out), None) == uf.UF_ERR_STATE
+        uf.uf_kvcache_append(h, None, None, 1, uf.UF_APPEND_COMMIT_ONLY, 0)
+        # 16 splits x 4100 queries x 16 heads x (128 + 2) x 4 bytes > 32 MiB
+        assert LIB.uf_attn_step_static(ctypes.byref(q), h, None, ctypes.byref(out), None) == uf.UF_ERR_CAPACITY
+        assert "scratch" in uf.uf_last_error()
+        assert LIB.uf_attn_step_static(ctypes.byref(q), h, None, ctypes.byref(q), None) == uf.UF_ERR_INVALID_ARG
+        assert LIB.uf_attn_step_static(ctypes.byref(q), None, None, ctypes.byref(out), None) == uf.UF_ERR_INVALID_ARG
+        bad = _tensor(4100, 16, data=FAKE * 32, dtype=3)
+        assert LIB.uf_attn_step_static(ctypes.byref(bad), h, None, ctypes.byref(out), None) == uf.UF_ERR_DTYPE
+    finally:
+        uf.uf_kvcache_destroy(h)
+    assert uf.UF_STATIC_SCRATCH_BYTES == 32 << 20
+
+
+@pytest.mark.skipif(_stub_launches() is None, reason="only with the host-only build (launch stubs)")
+def test_static_step_reaches_the_launchers():
+    # no workspace in the description: only the static entry point splits (attention + combine)
+    st, h = create(H=3, d=128, L=1200, W=3)
+    assert st == uf.UF_OK
+    try:
+        uf.uf_kvcache_append(h, None, None, 3, uf.UF_APPEND_COMMIT_ONLY, 0)
+        q, out = _tensor(1200, 12, data=FAKE * 32), _tensor(1200, 12, data=FAKE * 64)
+        n0 = _stub_launches()
+        assert LIB.uf_attn_step(ctypes.byref(q), h, None, ctypes.byref(out), None) == uf.UF_OK
+        assert _stub_launches() == n0 + 1          # no workspace: one launch, no split
+        assert LIB.uf_attn_step_static(ctypes.byref(q), h, None, ctypes.byref(out), None) == uf.UF_OK
+        assert _stub_launches() == n0 + 3          # split into the static scratch, then combined
+    finally:
+        uf.uf_kvcache_destroy(h)

@@ -13,6 +13,8 @@
 #include "uf.h"
 #include "uf_internal.h"
 
+static_assert(uf::kStaticScratchBytes == UF_STATIC_SCRATCH_BYTES, "scratch size and its header constant");
+
 struct uf_kvcache {
   uf_kvcache_desc d;
   int64_t frames;       // frames appended since create / reset
@@ -348,8 +350,15 @@ uf_status uf_kvcache_append(uf_kvcache* cache, const uf_tensor* k_new, const uf_
   return UF_OK;
 }
 
-uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mask* mask, uf_tensor* out,
-                       void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The attention step with split partials in `ws` (ws_bytes bytes, 256-byte aligned, or NULL
+// with 0).  With use_static, ws is ignored: the partials go to the library's own per-device
+// scratch, and a forced split count whose partials do not fit it is refused.
+uf_status attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mask* mask, uf_tensor* out,
+                    void* stream, void* ws, size_t ws_bytes, bool use_static) {
   if (!cache) return fail(UF_ERR_INVALID_ARG, "cache is NULL");
   const auto& d = cache->d;
   uf_status s;
@@ -417,11 +426,20 @@ uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mas
   }
   if (d.splits) splits = std::min(d.splits, n_kt);
   const int64_t rows = (int64_t)n_q * hq;
+  if (use_static) ws_bytes = uf::kStaticScratchBytes;
   const auto fits = [&](int s) {
-    return s == 1 || (int64_t)s * rows * (d.head_dim + 2) * (int64_t)sizeof(float) <= (int64_t)d.workspace_bytes;
+    return s == 1 || (int64_t)s * rows * (d.head_dim + 2) * (int64_t)sizeof(float) <= (int64_t)ws_bytes;
   };
+  if (use_static && d.splits && !fits(splits))
+    return fail(UF_ERR_CAPACITY, "%d splits of %lld (query, head) rows need %lld bytes of scratch; the library holds %zu",
+                splits, (long long)rows, (long long)splits * rows * (d.head_dim + 2) * (long long)sizeof(float),
+                uf::kStaticScratchBytes);
   while (splits > 1 && !fits(splits)) --splits;
   if (items * splits >= kMaxIndex) return fail(UF_ERR_CAPACITY, "grid too large");
+  if (use_static && splits > 1) {
+    hipError_t e = uf::static_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "scratch address");
+  }
 
   uf::AttnParams p;
   p.q = (const uint16_t*)q->data;
@@ -451,8 +469,8 @@ uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mas
   p.mask_stride_head = mask ? mask->stride_head : 0;
   p.mask_stride_q = mask ? mask->stride_qblock : 0;
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d.head_dim));
-  p.ws_o = (float*)d.workspace;
-  p.ws_ml = splits > 1 ? (float*)d.workspace + (size_t)splits * rows * d.head_dim : nullptr;
+  p.ws_o = splits > 1 ? (float*)ws : nullptr;
+  p.ws_ml = splits > 1 ? (float*)ws + (size_t)splits * rows * d.head_dim : nullptr;
   p.blk_h = d.block_grid_h;
   p.blk_w = d.block_grid_w;
   p.blk_frames = cache->block_frames;
@@ -482,6 +500,21 @@ uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mas
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
   return UF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uf_status uf_attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mask* mask, uf_tensor* out,
+                       void* stream) {
+  if (!cache) return fail(UF_ERR_INVALID_ARG, "cache is NULL");
+  return attn_step(q, cache, mask, out, stream, cache->d.workspace, cache->d.workspace_bytes, false);
+}
+
+uf_status uf_attn_step_static(const uf_tensor* q, uf_kvcache* cache, const uf_block_mask* mask, uf_tensor* out,
+                              void* stream) {
+  return attn_step(q, cache, mask, out, stream, nullptr, 0, true);
 }
 
 size_t uf_block_mask_workspace_bytes(const uf_kvcache_desc* desc, int32_t n_q_tokens, int32_t n_q_heads) {

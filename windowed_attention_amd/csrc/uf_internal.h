@@ -107,6 +107,12 @@ struct TopkParams {
 // Key tiles per row that the selection kernel holds in LDS (4 rows per work-group).
 constexpr int kTopkMaxKeyTiles = 3072;
 
+// Device memory of the allocation-free attention step: a file-scope array of
+// kStaticScratchBytes per device, held until the process ends.  static_scratch() returns its
+// device address on the current device (looked up once per device, then cached).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(void** ptr);
+
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);

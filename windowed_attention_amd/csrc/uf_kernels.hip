@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "uf_attn_walk.h"
 #include "uf_device.h"
 #include "uf_internal.h"
@@ -343,6 +345,37 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(CombineParams p) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free attention step (split partials), one copy per device.  In
+// host code `scratch` names a host-side stand-in, not the device array: its device address
+// comes from hipGetSymbolAddress, taken once per device with that device current, and only
+// that address is ever passed to a kernel.
+
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
   const uint32_t total = (uint32_t)p.n_tok * (uint32_t)(p.head_dim / 8) * (uint32_t)p.n_heads;

@@ -30,11 +30,13 @@ UF_APPEND_OVERWRITE_NEWEST = 1
 UF_APPEND_COMMIT_ONLY = 2
 UF_TILE = 128
 UF_MAX_APPEND_FRAMES = 64
+UF_STATIC_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = [
     "uf_kvcache_storage_bytes", "uf_attn_workspace_bytes", "uf_kvcache_create", "uf_kvcache_destroy",
     "uf_kvcache_reset", "uf_kvcache_set_window", "uf_kvcache_append", "uf_kvcache_plan_append",
-    "uf_kvcache_window", "uf_attn_step", "uf_block_mask_workspace_bytes", "uf_block_mask_topk",
+    "uf_kvcache_window", "uf_attn_step", "uf_attn_step_static", "uf_block_mask_workspace_bytes",
+    "uf_block_mask_topk",
     "uf_status_string", "uf_last_error",
 ]
 
@@ -101,6 +103,8 @@ def _load():
         "uf_kvcache_window": (ctypes.c_int, [ctypes.c_void_p, P(uf_window_info)]),
         "uf_attn_step": (ctypes.c_int, [P(uf_tensor), ctypes.c_void_p, P(uf_block_mask), P(uf_tensor),
                                         ctypes.c_void_p]),
+        "uf_attn_step_static": (ctypes.c_int, [P(uf_tensor), ctypes.c_void_p, P(uf_block_mask), P(uf_tensor),
+                                               ctypes.c_void_p]),
         "uf_block_mask_workspace_bytes": (ctypes.c_size_t, [P(uf_kvcache_desc), ctypes.c_int32, ctypes.c_int32]),
         "uf_block_mask_topk": (ctypes.c_int, [P(uf_tensor), ctypes.c_void_p, P(uf_topk_params), ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -208,6 +212,12 @@ def uf_attn_step(q, handle: int, block_mask, out, stream=None) -> None:
                              _stream_handle(stream)), "uf_attn_step")
 
 
+def uf_attn_step_static(q, handle: int, block_mask, out, stream=None) -> None:
+    m = None if block_mask is None else ctypes.byref(mask_of(block_mask))
+    _check(_lib.uf_attn_step_static(ctypes.byref(tensor_of(q)), handle, m, ctypes.byref(tensor_of(out)),
+                                    _stream_handle(stream)), "uf_attn_step_static")
+
+
 def uf_block_mask_workspace_bytes(desc: uf_kvcache_desc, n_q_tokens: int, n_q_heads: int) -> int:
     return _lib.uf_block_mask_workspace_bytes(ctypes.byref(desc), n_q_tokens, n_q_heads)
 
@@ -297,6 +307,10 @@ class KVCache:
 
     def attn_step(self, q, out, block_mask=None, stream=None):
         uf_attn_step(q, self.handle, block_mask, out, stream)
+        return out
+
+    def attn_step_static(self, q, out, block_mask=None, stream=None):
+        uf_attn_step_static(q, self.handle, block_mask, out, stream)
         return out
 
     def block_mask_topk(self, q, top_k: int, local_blocks: int = 0, mask=None, scores=None, workspace=None,
