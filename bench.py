@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense FP8 MFMA (twice the bf16 rate)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_2k_traffic.md")
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_kernel_2k_1k_mfma_counters.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_traffic.md")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_kernel_mfma_counters.md")
 CSRC = os.path.join(ROOT, "windowed_attention_amd", "csrc")
 # every source compiled into the bf16 attention kernel (its schedule lives in the headers)
 KERNEL_SOURCES = ["uf_kernels.hip", "uf_attn_walk.h", "uf_device.h", "uf_internal.h"]
@@ -429,8 +429,11 @@ def cpu_stream(cfg, budget_s=20.0):
     }
 
 
-def summary(r):
+def summary(r, profiled=True):
+    """The leg's figures; profiled=False for legs the committed bf16 profiles do not cover (FP8,
+    block order)."""
     cfg = r["cfg"]
+    traffic = measured_traffic(cfg.name) if profiled else None
     return {
         "workload": f"{cfg.name} chunk: {cfg.n_q_heads}x{cfg.head_dim} heads (KV {cfg.n_kv_heads}), "
                     f"{cfg.grid[0]}x{cfg.grid[1]} tokens/frame, {cfg.frames_per_step} frames/step, "
@@ -450,6 +453,10 @@ def summary(r):
         "append_gbs": r["append_gbs"],
         "append_frac_hbm": r["append_gbs"] / PEAK_HBM_GBS,
         "gflop_per_step": r["flops_per_step"] / 1e9,
+        # bf16 legs: HBM bytes per attention launch from the committed counter profile, over the
+        # algorithmic bytes (None when the profile is of other kernel sources)
+        "traffic_over_algorithmic": None if traffic is None else round(traffic / algorithmic_attn_bytes(cfg), 2),
+        "profiled_clock_ghz": profiled_clock(cfg.name) if profiled else None,
     }
 
 
@@ -505,14 +512,14 @@ def main():
     if not args.no_fp8 and cfg.head_dim in (64, 128):
         log(f"{cfg.name}: FP8 (E4M3) cache")
         r8 = run_workload(cfg, args.warmup, args.steps, fp8=True)
-        fp8 = summary(r8)
+        fp8 = summary(r8, profiled=False)
         fp8["scales_q_k_v"] = list(FP8_SCALES)
         fp8["peak_fp8_tflops"] = PEAK_FP8_TFLOPS
         fp8["pct_peak_fp8_attn_kernel"] = 100 * r8["attn_tflops"] / PEAK_FP8_TFLOPS
     blk = None
     if not args.no_block_order:
         log(f"{cfg.name}: (2,8,8) block order")
-        blk = summary(run_workload(cfg, args.warmup, args.steps, block_order=True))
+        blk = summary(run_workload(cfg, args.warmup, args.steps, block_order=True), profiled=False)
     topk = None
     if not args.no_topk and cfg.mask_pct is not None:
         log(f"{cfg.name}: top-k block-mask generation")
