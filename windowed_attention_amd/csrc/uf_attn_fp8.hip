@@ -258,15 +258,29 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
     f32x16 s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) s[kb] = f32x16{};
+    // MFMA m = 4c + kb takes the K fragment of d chunk c, key block kb.  Fragments are read two
+    // MFMAs ahead (a ring of three in registers), and the schedule below keeps that order: left
+    // to itself the compiler waits for each fragment right before its MFMA.
+    constexpr int NS = 4 * NCH;
+    auto kfrag = [&](int m) {
+      const int c = m / 4, kb = m % 4;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(tb + koff[c][0] + 32 * kb * RB);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(tb + koff[c][1] + 32 * kb * RB);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    i32x8 ka[3];
+    ka[0] = kfrag(0);
+    ka[1] = kfrag(1);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    for (int m = 0; m < NS; ++m) {
+      if (m + 2 < NS) ka[(m + 2) % 3] = kfrag(m + 2);
+      s[m % 4] = mfma8(ka[m % 3], qf[m / 4], s[m % 4]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the fragments of MFMAs 0 and 1
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(tb + koff[c][0] + 32 * kb * RB);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(tb + koff[c][1] + 32 * kb * RB);
-        const i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        s[kb] = mfma8(a, qf[c], s[kb]);
-      }
+    for (int m = 0; m < NS; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA m
+      if (m + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the fragment of MFMA m + 2
     }
     // accumulator j of key block kb holds key 32*kb + 16*(j/8) + 8*half + j%8
     if (nvalid < kTile) {
@@ -306,8 +320,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
                       __builtin_amdgcn_exp2f(__builtin_fmaf(blk[j + 3], c2, -mc)));
       }
       lacc = mfma8(ones, pf, lacc);
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
+      // V^T fragments one d block ahead of their MFMA (the same ordering trick as for K)
+      auto vfrag = [&](int db) {
         i32x8 a;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -316,7 +330,24 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
           a[2 * r] = v[0];
           a[2 * r + 1] = v[1];
         }
-        o[db] = mfma8(a, pf, o[db]);
+        return a;
+      };
+      i32x8 va[3];
+      va[0] = vfrag(0);
+      if (ND > 1) va[1] = vfrag(1);
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        if (db + 2 < ND) va[(db + 2) % 3] = vfrag(db + 2);
+        o[db] = mfma8(va[db % 3], pf, o[db]);
+      }
+      // reads of d blocks 0 and 1, the row-sum MFMA and the MFMA of block 0, then per block the
+      // reads two ahead and its MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, ND > 1 ? 8 : 4, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+#pragma unroll
+      for (int db = 1; db < ND; ++db) {
+        if (db + 1 < ND) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       }
     }
   };

@@ -208,13 +208,28 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
     f32x16 s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) s[kb] = f32x16{};
+    // The K fragments of d chunk c + 1 are read while chunk c multiplies (two chunks in
+    // registers), and the schedule below keeps the reads two chunks ahead of the MFMAs: left
+    // to itself the compiler reads one fragment at a time into one register quad and waits
+    // for each read before its MFMA.
+    bf16x8 a[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) a[0][kb] = *reinterpret_cast<const bf16x8*>(smem + koff[0] + 32 * kb * RB);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      bf16x8 a[4];
+      if (c + 1 < NC) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) a[kb] = *reinterpret_cast<const bf16x8*>(smem + koff[c] + 32 * kb * RB);
+        for (int kb = 0; kb < 4; ++kb)
+          a[(c + 1) & 1][kb] = *reinterpret_cast<const bf16x8*>(smem + koff[c + 1] + 32 * kb * RB);
+      }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qf[c], s[kb], 0, 0, 0);
+      for (int kb = 0; kb < 4; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c & 1][kb], qf[c], s[kb], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads of chunks 0 and 1
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                     // the MFMAs of chunk c
+      if (c + 2 < NC) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // the reads of chunk c + 2
     }
     // accumulator j of key block kb holds key 32*kb + 16*(j/8) + 8*half + j%8
     if (nvalid < kTile) {
