@@ -74,3 +74,47 @@ def test_captured_step_replays_bit_exact(kind):
         assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), f"replay {r}: output differs"
         _ = (torch.ones(1000, device="cuda:0") * r).sum().item()  # eager work between replays
     cache.close()
+
+
+@pytest.mark.parametrize("entry", ["attn_step", "attn_step_static"])
+def test_captured_split_step_merges_on_every_replay(entry):
+    """A step whose key range is split (attention parts, then the combine kernel) captured as
+    the cache's first step, replayed with eager split steps in between, through the workspace
+    and through the static scratch.  Every replay and every eager step must equal the eager
+    result of a twin cache bit for bit."""
+    cfg = Workload(51, "g-split", "bf16", 8, 2, 128, (12, 25), 1, 3, 0, 4, None)
+    F = cfg.frames_per_step
+    mk = lambda: KVCache(cfg.n_kv_heads, cfg.head_dim, cfg.tokens_per_frame, cfg.window_frames, 0, splits=3)
+    cache, twin = mk(), mk()
+    dev = [tuple(to_dev(x) for x in draw_step_tensors(cfg, s)) for s in range(cfg.steps)]
+    for s in range(cfg.steps):
+        for c in (cache, twin):
+            c.append(dev[s][1], dev[s][2], F)
+    q = dev[-1][0]
+    out_e = torch.empty_like(q)
+    twin.attn_step(q, out_e)
+    torch.cuda.synchronize()
+    call = getattr(cache, entry)
+
+    out_g = torch.zeros_like(q)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            call(q, out_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out_g.fill_(0)
+        torch.cuda.synchronize()
+        print(f"{entry}: replay {r}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), f"replay {r}: output differs"
+        out_x = torch.full_like(q, 5.0)
+        call(q, out_x)   # eager split steps between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(out_x.view(torch.int16), out_e.view(torch.int16)), f"eager step after replay {r} differs"
+    cache.close()
+    twin.close()
