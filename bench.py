@@ -13,8 +13,9 @@ step (append included), timed over --steps steady steps (default 300, about
 from HIP events on the launch stream; `cpu_baseline` times the float64 oracle
 on the host's cores (its affinity mask): a bounded sample of the same step,
 and the tiny, 480P and decoder streams from their first step (each bounded).
-`also` repeats the step measurement for the 1K, 480P, decoder and
-FlashDecoder-XL workloads (at least --also-seconds of GPU time each); `fp8`,
+`also` repeats the step measurement for the tiny, 1K, 480P, decoder and
+FlashDecoder-XL workloads (at least --also-seconds of GPU time each, at most
+20000 steps); `fp8`,
 `block_order`, `mask_topk` and `mask_topk_gqa` are the FP8 cache, the (2,8,8)
 block order and block-mask generation legs.
 """
@@ -210,7 +211,7 @@ def run_workload(cfg, warmup, steps, fp8=False, block_order=False, min_seconds=0
             one_step(pool[steady[i % len(steady)]])
         torch.cuda.synchronize()
         per_step = (time.perf_counter() - t) / 10
-        steps = max(steps, int(min_seconds / per_step) + 1)
+        steps = max(steps, min(20000, int(min_seconds / per_step) + 1))
 
     log(f"{cfg.name}: timing {steps} steps")
     seq = [steady[i % len(steady)] for i in range(steps)]
@@ -465,7 +466,7 @@ def algorithmic_attn_bytes(cfg):
     return 2 * cfg.head_dim * (2 * cfg.q_tokens * cfg.n_q_heads + 2 * steady_keys(cfg) * cfg.n_kv_heads)
 
 
-DEFAULT_ALSO = "1k,480p,decoder,decoder-xl,refine-xl"
+DEFAULT_ALSO = "tiny,1k,480p,decoder,decoder-xl,refine-xl"
 
 
 def main():
@@ -539,6 +540,10 @@ def main():
         fill, _ = pool_size(cfg)
         cpu = cpu_baseline(cfg, fill, args.cpu_budget)
         cpu["streams"] = {n: cpu_stream(by_name[n], args.cpu_stream_budget) for n in ("tiny", "480p", "decoder")}
+        # the other chunk shape of the metric: one steady step, bounded like the main one
+        if cfg.name != "1k":
+            c1k = by_name["1k"]
+            cpu["other_steps"] = {"1k": cpu_baseline(c1k, pool_size(c1k)[0], args.cpu_budget)}
 
     s = summary(main_r)
     traffic_bytes = measured_traffic(cfg.name)
