@@ -204,11 +204,12 @@ size_t uf_kvcache_storage_bytes(const uf_kvcache_desc* desc);
 
 /* Workspace bytes that let every step split its key range as the library
  * would choose: (head_dim + 2) * 4 bytes per (split, query, head) row, for
- * at most 256 rows per compute unit of the current device (the library
- * splits only steps with fewer work items than two per compute unit, so
- * this never limits its own choice), and at most 16 * max_q_heads *
- * max_q_tokens rows when both are given.  A forced split count (desc
- * splits) that would need more is lowered to what fits.  0 if invalid. */
+ * at most 1024 rows per compute unit of the current device (the library
+ * splits only steps with fewer than two rounds of work-groups, into at most
+ * four rounds, so this never limits its own choice), and at most
+ * 16 * max_q_heads * max_q_tokens rows when both are given.  A smaller
+ * workspace means fewer splits; a forced split count (desc splits) that
+ * would need more is lowered to what fits.  0 if invalid. */
 size_t uf_attn_workspace_bytes(const uf_kvcache_desc* desc);
 
 /* Validate desc and create a handle with no frames appended.  The storage

@@ -89,9 +89,10 @@ def test_sizes():
     assert uf.uf_kvcache_storage_bytes(d) == 3 * 2 * 1560 * 128 * 2
     d = desc(H=12, d=128, L=1560, W=9, A=3)
     assert uf.uf_kvcache_storage_bytes(d) == 12 * 12 * 1560 * 128 * 2
-    # without a GPU the library assumes 256 compute units: 2 * 256 * 128 (split, query, head) rows
+    # without a GPU the library assumes 256 compute units: 4 rounds of 2 * 256 work-groups of
+    # 128 (split, query, head) rows
     full = uf.uf_attn_workspace_bytes(d)
-    assert full == 2 * 256 * 128 * (128 + 2) * 4
+    assert full == 4 * 2 * 256 * 128 * (128 + 2) * 4
     # with the step's largest size given, at most 16 splits of it
     assert uf.uf_attn_workspace_bytes(desc(H=3, d=64, L=1560, W=2, max_q_heads=12, max_q_tokens=100)) == \
         16 * 12 * 100 * (64 + 2) * 4

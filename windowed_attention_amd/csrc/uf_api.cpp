@@ -179,14 +179,39 @@ int device_cu_count() {
   return cached_cus;
 }
 
-// Split partials are budgeted in (split, query, head) rows.  The library splits a step only
-// when it has fewer work items (128 rows each) than two per compute unit, and then into at
-// most 2 * CUs / items parts, so it never needs more than 2 * CUs * 128 rows.
+// Split partials are budgeted in (split, query, head) rows.  The library's split rule
+// (choose_splits) never makes more than four rounds of resident work-groups (2 per CU) out of
+// the split work items, 128 rows each, so it never needs more than 4 * 2 * CUs * 128 rows.
 int64_t split_row_budget(const uf_kvcache_desc& d) {
-  int64_t rows = 2 * (int64_t)device_cu_count() * UF_TILE;
+  int64_t rows = 4 * 2 * (int64_t)device_cu_count() * UF_TILE;
   if (d.max_q_heads > 0 && d.max_q_tokens > 0)
     rows = std::min<int64_t>(rows, (int64_t)kMaxSplits * d.max_q_heads * d.max_q_tokens);
   return rows;
+}
+
+// Key-range parts for a step of `items` work items over n_kt key tiles, on a chip that holds
+// `slots` work-groups at once (two per CU), at least 4 key tiles per part.
+// - Fewer items than slots: as many parts as keep the whole grid resident (one more part
+//   starts a second round of work-groups, which costs more than the shorter ranges save:
+//   decoder 3 parts 62 us, 4 parts 74 us).
+// - Between one and two rounds of items: the last round runs mostly empty, because items of a
+//   dense step take about the same time.  Split into the parts (at most 4, at most 4 rounds)
+//   that fill the rounds best, when that fills them at least a tenth better than unsplit:
+//   decoder-XL (678 items, 1.32 rounds) 3 parts, 209 us instead of 245.
+// - Two rounds or more: unsplit.  Item times spread enough that the last round is not the
+//   problem, and partials cost more than they save (1K 2 parts 1.16 ms instead of 1.05).
+int choose_splits(int64_t items, int n_kt, int64_t slots) {
+  const int most = std::max(1, n_kt / 4);
+  if (items < slots) return (int)std::min<int64_t>({std::max<int64_t>(1, slots / items), kMaxSplits, most});
+  if (items >= 2 * slots) return 1;
+  const auto fill = [&](int s) {
+    const int64_t wgs = items * s;
+    return (double)wgs / (double)(((wgs + slots - 1) / slots) * slots);
+  };
+  int best = 1;
+  for (int s = 2; s <= std::min(4, most); ++s)
+    if (items * s <= 4 * slots && fill(s) > fill(best) + 1e-9) best = s;
+  return fill(best) >= fill(1) + 0.1 ? best : 1;
 }
 
 // The crop of a block-order stream must keep whole steps: every frame slot of a step holds
@@ -414,16 +439,7 @@ uf_status attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mask* 
   const int n_hgrp = hq / hpw;
   const int64_t items = (int64_t)n_qblk * n_hgrp;
 
-  // Split the key range when the work items alone leave CUs idle: as many splits as keep the
-  // whole grid resident at once (two work-groups per CU), at least 4 key tiles per split.
-  // One more split than that starts a second round of work-groups, which costs more than the
-  // shorter key ranges save (measured on the decoder shape: 3 splits 62 us, 4 splits 74 us).
-  int splits = 1;
-  const int cus = device_cu_count();
-  if (items < 2 * cus) {
-    splits = (int)std::min<int64_t>(std::max<int64_t>(1, (2 * cus) / items), kMaxSplits);
-    splits = std::min(splits, std::max(1, n_kt / 4));
-  }
+  int splits = choose_splits(items, n_kt, 2 * (int64_t)device_cu_count());
   if (d.splits) splits = std::min(d.splits, n_kt);
   const int64_t rows = (int64_t)n_q * hq;
   if (use_static) ws_bytes = uf::kStaticScratchBytes;

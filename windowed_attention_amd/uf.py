@@ -262,10 +262,11 @@ class KVCache:
                  anchor_frames: int = 0, device="cuda", workspace: bool = True, kv_dtype: int = UF_BF16,
                  q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0, block_grid=(0, 0),
                  max_q_heads: int = 0, max_q_tokens: int = 0, heads_per_wg: int = 0, splits: int = 0,
-                 k_storage=None, v_storage=None):
+                 k_storage=None, v_storage=None, workspace_bytes: int = None):
         """k_storage / v_storage: caller-made device tensors of the storage's shape
         [n_kv_heads, (anchor_frames + window_frames) * tokens_per_frame, head_dim] (bf16, or uint8
-        for FP8), e.g. views into larger buffers; allocated here when not given."""
+        for FP8), e.g. views into larger buffers; allocated here when not given.
+        workspace_bytes: size of the workspace allocated here (default: uf_attn_workspace_bytes)."""
         import torch
         desc = uf_kvcache_desc(n_kv_heads, head_dim, tokens_per_frame, window_frames, anchor_frames,
                                None, None, None, 0, kv_dtype, q_scale, k_scale, v_scale,
@@ -281,7 +282,7 @@ class KVCache:
                 raise ValueError(f"storage must be a contiguous {tdt} tensor of shape {shape}")
         self.k_storage = torch.empty(shape, dtype=tdt, device=device) if k_storage is None else k_storage
         self.v_storage = torch.empty_like(self.k_storage) if v_storage is None else v_storage
-        ws_bytes = uf_attn_workspace_bytes(desc) if workspace else 0
+        ws_bytes = (uf_attn_workspace_bytes(desc) if workspace_bytes is None else workspace_bytes) if workspace else 0
         self.workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
         desc.k_storage = self.k_storage.data_ptr()
         desc.v_storage = self.v_storage.data_ptr()
