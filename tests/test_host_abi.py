@@ -489,3 +489,26 @@ def test_static_step_reaches_the_launchers():
         assert _stub_launches() == n0 + 3          # split into the static scratch, then combined
     finally:
         uf.uf_kvcache_destroy(h)
+
+
+@pytest.mark.skipif(_stub_launches() is None, reason="only with the host-only build (launch stubs)")
+def test_split_rule_dense_and_masked():
+    """Decoder-XL shape (24 heads of 64 over 3 KV heads, 45x80 tokens per frame, 2 frames):
+    678 work items fill 1.3 rounds of 512 resident work-groups, so a dense step is split (the
+    attention launch and the combine); the same step under a block mask is not."""
+    L, H, HQ, d = 45 * 80, 3, 24, 64
+    ws_bytes = uf.uf_attn_workspace_bytes(desc(H=H, d=d, L=L, W=2))
+    st, h = create(H=H, d=d, L=L, W=2, ws=FAKE * 1024, ws_bytes=ws_bytes)
+    assert st == uf.UF_OK, uf.uf_last_error()
+    try:
+        uf.uf_kvcache_append(h, None, None, 2, uf.UF_APPEND_COMMIT_ONLY, 0)
+        q, out = _tensor(L, HQ, d=d, data=FAKE * 32), _tensor(L, HQ, d=d, data=FAKE * 64)
+        nqb, nkb = -(-L // 128), -(-2 * L // 128)
+        for m, launches in ((None, 2), (_mask(1, nqb, nkb), 1), (_mask(HQ, nqb, nkb), 1)):
+            n0 = _stub_launches()
+            got = LIB.uf_attn_step(ctypes.byref(q), h, ctypes.byref(m) if m is not None else None,
+                                   ctypes.byref(out), None)
+            assert got == uf.UF_OK, uf.uf_last_error()
+            assert _stub_launches() == n0 + launches
+    finally:
+        uf.uf_kvcache_destroy(h)

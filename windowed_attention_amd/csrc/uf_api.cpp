@@ -194,16 +194,18 @@ int64_t split_row_budget(const uf_kvcache_desc& d) {
 // - Fewer items than slots: as many parts as keep the whole grid resident (one more part
 //   starts a second round of work-groups, which costs more than the shorter ranges save:
 //   decoder 3 parts 62 us, 4 parts 74 us).
-// - Between one and two rounds of items: the last round runs mostly empty, because items of a
-//   dense step take about the same time.  Split into the parts (at most 4, at most 4 rounds)
-//   that fill the rounds best, when that fills them at least a tenth better than unsplit:
-//   decoder-XL (678 items, 1.32 rounds) 3 parts, 209 us instead of 245.
+// - Between one and two rounds of items of a dense step: the last round runs mostly empty,
+//   because items of a dense step take about the same time.  Split into the parts (at most 4,
+//   at most 4 rounds) that fill the rounds best, when that fills them at least a tenth better
+//   than unsplit: decoder-XL (678 items, 1.32 rounds) 3 parts, 209 us instead of 245.  Under
+//   a block mask the items keep different numbers of tiles and do not run in rounds: unsplit
+//   (decoder-XL under per-head top-k masks, 14 of 57 tiles kept: 3 parts 89 us, unsplit 71).
 // - Two rounds or more: unsplit.  Item times spread enough that the last round is not the
 //   problem, and partials cost more than they save (1K 2 parts 1.16 ms instead of 1.05).
-int choose_splits(int64_t items, int n_kt, int64_t slots) {
+int choose_splits(int64_t items, int n_kt, int64_t slots, bool masked) {
   const int most = std::max(1, n_kt / 4);
   if (items < slots) return (int)std::min<int64_t>({std::max<int64_t>(1, slots / items), kMaxSplits, most});
-  if (items >= 2 * slots) return 1;
+  if (masked || items >= 2 * slots) return 1;
   const auto fill = [&](int s) {
     const int64_t wgs = items * s;
     return (double)wgs / (double)(((wgs + slots - 1) / slots) * slots);
@@ -439,7 +441,7 @@ uf_status attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mask* 
   const int n_hgrp = hq / hpw;
   const int64_t items = (int64_t)n_qblk * n_hgrp;
 
-  int splits = choose_splits(items, n_kt, 2 * (int64_t)device_cu_count());
+  int splits = choose_splits(items, n_kt, 2 * (int64_t)device_cu_count(), mask != nullptr);
   if (d.splits) splits = std::min(d.splits, n_kt);
   const int64_t rows = (int64_t)n_q * hq;
   if (use_static) ws_bytes = uf::kStaticScratchBytes;
