@@ -213,7 +213,10 @@ size_t uf_kvcache_storage_bytes(const uf_kvcache_desc* desc);
 size_t uf_attn_workspace_bytes(const uf_kvcache_desc* desc);
 
 /* Validate desc and create a handle with no frames appended.  The storage
- * contents are not touched.  *out is set only on UF_OK. */
+ * contents are not touched.  *out is set only on UF_OK.  UF_ERR_CAPACITY when
+ * one head's K (or V) storage, (anchor_frames + window_frames) x tokens_per_frame
+ * rows of head_dim elements, reaches 4 GiB: the kernels address it with 32-bit
+ * byte offsets. */
 uf_status uf_kvcache_create(const uf_kvcache_desc* desc, uf_kvcache** out);
 
 /* Free the handle (NULL is accepted).  The caller frees the device memory. */

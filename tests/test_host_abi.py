@@ -70,6 +70,7 @@ def create(**kw):
     (dict(ws_bytes=1024), uf.UF_ERR_INVALID_ARG),          # size without a pointer
     (dict(ws=FAKE * 8 + 16, ws_bytes=1024), uf.UF_ERR_INVALID_ARG),  # misaligned workspace
     (dict(L=1 << 20, W=4096), uf.UF_ERR_CAPACITY),
+    (dict(L=1 << 20, W=16), uf.UF_ERR_CAPACITY),           # 2^24 rows of 256 bytes: 4 GiB per head
     (dict(hpw=3), uf.UF_ERR_INVALID_ARG),
     (dict(hpw=8), uf.UF_ERR_INVALID_ARG),
     (dict(splits=17), uf.UF_ERR_INVALID_ARG),
@@ -512,3 +513,16 @@ def test_split_rule_dense_and_masked():
             assert _stub_launches() == n0 + launches
     finally:
         uf.uf_kvcache_destroy(h)
+
+
+def test_largest_head_storage_is_accepted():
+    """Just under 4 GiB of K per head (bf16) is accepted, and so are 2^24 rows of E4M3 codes
+    (2 GiB), whose bf16 twin is refused."""
+    st, h = create(L=1 << 20, W=15)
+    assert st == uf.UF_OK, uf.uf_last_error()
+    uf.uf_kvcache_destroy(h)
+    dd = desc(L=1 << 20, W=16)
+    dd.kv_dtype, dd.q_scale, dd.k_scale, dd.v_scale = uf.UF_FP8_E4M3, 1.0, 1.0, 1.0
+    hh = ctypes.c_void_p()
+    assert LIB.uf_kvcache_create(ctypes.byref(dd), ctypes.byref(hh)) == uf.UF_OK, uf.uf_last_error()
+    uf.uf_kvcache_destroy(hh.value)

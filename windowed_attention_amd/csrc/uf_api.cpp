@@ -52,9 +52,11 @@ uf_status check_desc(const uf_kvcache_desc* d) {
   if (d->tokens_per_frame < 1) return fail(UF_ERR_SHAPE, "tokens_per_frame must be >= 1");
   if (d->window_frames < 1) return fail(UF_ERR_SHAPE, "window_frames must be >= 1");
   if (d->anchor_frames < 0) return fail(UF_ERR_SHAPE, "anchor_frames must be >= 0");
+  // the attention kernels address a head's K or V storage with 32-bit byte offsets
   const int64_t rows = (int64_t)(d->anchor_frames + (int64_t)d->window_frames) * d->tokens_per_frame;
-  if (rows >= kMaxIndex || rows * d->head_dim >= kMaxIndex * 64)
-    return fail(UF_ERR_CAPACITY, "cache of %lld rows per head is too large", (long long)rows);
+  if (rows >= kMaxIndex || rows * d->head_dim * (d->kv_dtype == UF_FP8_E4M3 ? 1 : 2) >= ((int64_t)1 << 32))
+    return fail(UF_ERR_CAPACITY, "cache of %lld rows per head is too large (at most 4 GiB per head and tensor)",
+                (long long)rows);
   if ((d->block_grid_h == 0) != (d->block_grid_w == 0) || d->block_grid_h < 0 || d->block_grid_w < 0 ||
       (d->block_grid_h && (int64_t)d->block_grid_h * d->block_grid_w != d->tokens_per_frame))
     return fail(UF_ERR_SHAPE, "block grid %d x %d does not give %d tokens per frame", d->block_grid_h,

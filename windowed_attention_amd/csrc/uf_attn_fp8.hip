@@ -98,39 +98,10 @@ __global__ void __launch_bounds__(kThreads) append_fp8_kernel(AppendFp8Params p)
 
 // ---------------------------------------------------------------------------
 // Attention.  Work-group and schedule as in the bf16 kernel: 4 waves, 128 (query, head)
-// rows, one wave per 32-query row block, two work-groups per CU.  FP8 tiles are half the
-// bytes of bf16 ones, so each work-group double-buffers its K and V tiles in the same LDS
-// the bf16 kernel single-buffers in: the copy of the next kept tile runs under the
-// computation of the current one.
-
-// Global -> LDS copy of 16 bytes per lane (lane i's bytes land at lds_dst + 16 i), as inline
-// asm: the instruction has no register result, and written this way the compiler does not
-// take it for an LDS store that every later LDS read must wait for, which would hold the
-// reads of the current tile until the next tile's copy has landed.  The callers wait for
-// the copies themselves (s_waitcnt vmcnt(0) before the barrier that publishes a tile).
-// The LDS address goes in M0, which the compiler reserves: each statement saves M0 in a
-// scratch SGPR and restores it after the instruction has issued.
-__device__ inline void copy16_async(const void* src, void* lds_dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(UF_LDS void*)lds_dst);
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "s"(lds), "v"(src)
-               : "memory");
-}
-// The same from a wave-uniform base plus a 32-bit per-lane byte offset (the scalar-base
-// form of the instruction: no per-lane 64-bit address arithmetic).
-__device__ inline void copy16_async(const void* base, uint32_t off, void* lds_dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(UF_LDS void*)lds_dst);
-  const uint64_t b = (uint64_t)(uintptr_t)base;
-  const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "s"(lds), "v"(off), "s"(sb)
-               : "memory");
-}
+// rows, one wave per 32-query row block, two work-groups per CU, K and V double-buffered in
+// 64 KB of LDS.  FP8 tiles are half the bytes of bf16 ones, so the buffers hold whole
+// 128-key tiles (the bf16 kernel's hold 64-key sub-tiles): the copy of the next kept tile
+// runs under the computation of the current one.
 
 // 16-byte chunk swizzle of LDS row r (rows of D bytes): chunk c sits at c ^ swz(r), which
 // spreads both the 16-lane row-strided K reads and the 8-row transpose reads of V over

@@ -5,7 +5,6 @@
 #include <stdint.h>
 
 #define UF_LDS __attribute__((address_space(3)))
-#define UF_GLOBAL __attribute__((address_space(1)))
 
 namespace uf {
 
@@ -49,11 +48,35 @@ __device__ inline float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Asynchronous copy of 16 bytes per lane from global memory into LDS (lane i's bytes land
-// at lds_dst + 16 i); completion is counted by vmcnt.
-__device__ inline void load_lds16(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds((const UF_GLOBAL void*)src, (UF_LDS void*)lds_dst, 16, 0, 0);
+// Global -> LDS copy of 16 bytes per lane (lane i's bytes land at lds_dst + 16 i), as inline
+// asm: the instruction has no register result, and written this way the compiler does not
+// take it for an LDS store that every later LDS read must wait for, which would hold the
+// reads of the current tile until the next tile's copy has landed.  The callers wait for
+// the copies themselves (s_waitcnt vmcnt(0) before the barrier that publishes a tile).
+// The LDS address goes in M0, which the compiler reserves: each statement saves M0 in a
+// scratch SGPR and restores it after the instruction has issued.
+__device__ inline void copy16_async(const void* src, void* lds_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(UF_LDS void*)lds_dst);
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds), "v"(src)
+               : "memory");
 }
+// The same from a wave-uniform base plus a 32-bit per-lane byte offset (the scalar-base
+// form of the instruction: no per-lane 64-bit address arithmetic).
+__device__ inline void copy16_async(const void* base, uint32_t off, void* lds_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(UF_LDS void*)lds_dst);
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds), "v"(off), "s"(sb)
+               : "memory");
+}
+
 
 // Raster token (frame f, row y, column x -> (f H + y) W + x) at position i of a step's
 // block order, for F frames of an H x W grid (Ultra Flash notes, key design 3: (2,8,8)

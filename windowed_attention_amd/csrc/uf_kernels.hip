@@ -58,11 +58,14 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendParams p) {
 //
 // Work-group: 4 waves, 128 (query, head) rows = 4 row blocks of 32 queries
 // of one query head, one wave per row block; two work-groups share a CU.
-// Per kept key tile (128 keys) the work-group stages K and V straight from
-// global memory into LDS (global_load_lds, 16 bytes per lane, no register
-// staging) and every wave computes its 32 rows against all 128 keys.  The
-// LDS tile is single-buffered: while one work-group of a CU waits for its
-// next tile, the other computes.
+// Each kept key tile (128 keys) is taken as two 64-key sub-tiles.  The
+// work-group stages K and V of a sub-tile straight from global memory into
+// LDS (global_load_lds, 16 bytes per lane, no register staging) and every
+// wave computes its 32 rows against its 64 keys.  K and V are double-
+// buffered: two sub-tile buffers of 32 KB, the 64 KB one 128-key tile would
+// take, so that two work-groups still share a CU.  The copy of sub-tile
+// j + 1 goes out during the S MFMAs of sub-tile j and is waited for at the
+// end of step j.
 //
 //   S^T = K . Q^T     mfma 32x32x16 bf16: A = K rows (LDS), B = Q^T (registers)
 //   online softmax    fp32 per query (= per lane % 32); rescaling of the
@@ -102,29 +105,28 @@ __device__ __forceinline__ int swz(int row) {
 
 constexpr int kAttnThreads = 256;  // 4 waves; two work-groups per CU
 
+constexpr int kSub = 64;  // keys per sub-tile: two per key tile
+
 template <int D>
 __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
   constexpr int NC = D / 16;            // 16-wide d chunks of the S^T mfma
   constexpr int ND = D / 32;            // 32-row d blocks of O^T
   constexpr int CPR = D / 8;            // 16-byte chunks per LDS row
   constexpr int RB = D * 2;             // bytes per LDS row
-  constexpr int TILE_B = kTile * RB;    // bytes per K (or V) tile
+  constexpr int SUB_B = kSub * RB;      // bytes per K (or V) sub-tile
   constexpr int RPI = 64 / CPR;         // rows written by one wave-wide 16-byte load
-  constexpr int NW = kAttnThreads / 64; // waves
-  constexpr int NLD = kTile / RPI / NW; // such loads per wave, per tensor and tile
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_B];  // [K tile][V tile]
+  constexpr int NLD = 16 / RPI;         // such loads per wave, per tensor and sub-tile (16 rows)
+  __shared__ __attribute__((aligned(1024))) char smem[4 * SUB_B];  // [K0][V0][K1][V1]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int rb = wave;  // row block
+  const int rb = wave;
 
-  // ---- work item
   const AttnItem it = attn_item(p, blockIdx.x, gridDim.x, rb, l32);
   const int head = it.head, kvh = it.kvh, qi = it.qi, qt = it.qt;
 
-  // ---- Q^T fragments (B operand), in registers for the whole key range
   bf16x8 qf[NC];
   {
     const bool ok = qi < p.n_q;
@@ -140,108 +142,108 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
   f32x16 o[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY;  // reference max (raw score units) of this lane's query
-  float l_run = 0.f;        // this lane half's sum of probabilities
+  float m_run = -INFINITY;
+  float l_run = 0.f;
   const float c2 = p.scale_log2;
   const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)kvh * p.kv_head_stride;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)kvh * p.kv_head_stride;
-  KeyTiles tiles(p, it);  // the kept key tiles, ascending
+  KeyTiles tiles(p, it);
 
-  // K and V of tile kt -> LDS (asynchronous; completion via vmcnt).  Lane
-  // element offsets for a tile whose 128 keys are 128 consecutive storage
-  // rows (every full tile that does not cross the anchor/ring boundary or
-  // the ring's wrap): the tile is then one scalar base plus these offsets.
-  uint32_t lane_off[NLD];
+  // This wave copies rows 16 wave .. + 15 of every K and V sub-tile.
+  const int row0 = 16 * wave;
+  uint32_t lane_off[NLD];  // byte offsets within a sub-tile of 64 consecutive storage rows
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
-    const int row = (wave * NLD + i) * RPI + lane / CPR;
-    lane_off[i] = row * D + ((lane % CPR) ^ swz<D>(row)) * 8;
+    const int row = row0 + i * RPI + lane / CPR;
+    lane_off[i] = (uint32_t)(row * D + ((lane % CPR) ^ swz<D>(row)) * 8) * 2u;
   }
-  auto issue = [&](int kt) {
-    const int j0 = kt * kTile;
-    const int nvalid = min(kTile, p.n_k - j0);
-    char* kd = smem + wave * NLD * 1024;
-    char* vd = kd + TILE_B;
-    const int r0 = contiguous_tile_rows(p, kt);
-    if (r0 >= 0) {
-      const __bf16* kt_base = kbase + (int64_t)r0 * D;
-      const __bf16* vt_base = vbase + (int64_t)r0 * D;
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        load_lds16(kt_base + lane_off[i], kd + i * 1024);
-        load_lds16(vt_base + lane_off[i], vd + i * 1024);
-      }
-    } else {  // partial tile, or one that straddles the anchor/ring boundary or the wrap
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int row = (wave * NLD + i) * RPI + lane / CPR;
-        const int chunk = (lane % CPR) ^ swz<D>(row);
-        const int64_t off = (int64_t)key_row(p, j0 + min(row, nvalid - 1)) * D + chunk * 8;
-        load_lds16(kbase + off, kd + i * 1024);
-        load_lds16(vbase + off, vd + i * 1024);
+  // Byte offsets, from the head's base, of this wave's copy rows of the sub-tile starting at
+  // key j0 (the same for K and V); j0 < 0 gives row 0 of the head, a harmless copy into a
+  // buffer that is not read again.  (The host keeps a head's storage under 4 GB.)
+  auto copy_offsets = [&](int j0, uint32_t (&off)[NLD]) {
+    int r0 = -1;
+    if (j0 >= 0 && p.n_k - j0 >= kSub) {
+      if (j0 + kSub <= p.anchor_keys) {
+        r0 = j0;
+      } else if (j0 >= p.anchor_keys) {
+        int r = j0 - p.anchor_keys + p.ring_rot;
+        if (r >= p.ring_cap) r -= p.ring_cap;
+        if (r + kSub <= p.ring_cap) r0 = p.ring_base + r;
       }
     }
-  };
-  // Per-lane LDS byte offsets of the fragment reads.  Every other term of an
-  // address (key block, key chunk) is a multiple of 16 rows, leaves the
-  // swizzle unchanged and goes into the instruction's immediate offset.
-  uint32_t koff[NC];  // K rows for S^T: row 32*kb + rowperm(l32), chunk 2c + half
+    if (r0 >= 0) {
+      const uint32_t b = (uint32_t)r0 * (uint32_t)RB;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int r = rowperm(l32);
-    koff[c] = r * RB + (((2 * c + half) ^ swz<D>(r)) << 4);
-  }
-  uint32_t voff[ND][2];  // V rows for the transpose reads: key 16t + 8*half + 4*sub + (lane&15)/4
+      for (int i = 0; i < NLD; ++i) off[i] = b + lane_off[i];
+    } else if (j0 >= 0) {
+      const int nvalid = min(kSub, p.n_k - j0);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int row = row0 + i * RPI + lane / CPR;
+        const int chunk = (lane % CPR) ^ swz<D>(row);
+        off[i] = ((uint32_t)key_row(p, j0 + min(row, nvalid - 1)) * D + chunk * 8) * 2u;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) off[i] = (uint32_t)(lane % CPR) * 16u;
+    }
+  };
+  // K rows for S^T: row 32 kb + rowperm(l32), chunk 2c + half at position (half ^ swz) ^ 2c
+  const uint32_t koff0 = rowperm(l32) * RB + ((half ^ swz<D>(rowperm(l32))) << 4);
+  uint32_t voff[ND][2];  // V rows: key 16 t + 8 half + 4 sub + (lane & 15) / 4
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int key = 8 * half + 4 * sub + ((lane & 15) >> 2);
       const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      voff[db][sub] = TILE_B + key * RB + ((((col >> 3) ^ swz<D>(key)) << 4) | ((col & 7) << 1));
+      voff[db][sub] = SUB_B + key * RB + ((((col >> 3) ^ swz<D>(key)) << 4) | ((col & 7) << 1));
     }
   typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
   const bf16x2v ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // one tile in LDS: S^T = K Q^T (4 blocks of 32 keys), softmax, O^T += V^T P^T
-  auto compute = [&](int nvalid) {
-    f32x16 s[4];
+  // one sub-tile in buffer tb: S^T = K Q^T (2 blocks of 32 keys), softmax, O^T += V^T P^T;
+  // the copies of the next sub-tile (offsets ko, into buffer nb) go out during the S MFMAs
+  auto compute = [&](int nvalid, const char* tb, char* nb, const uint32_t (&ko)[NLD]) {
+    f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    bf16x8 a[3][2];
+    auto kfrag = [&](int c, int kb) {
+      return *reinterpret_cast<const bf16x8*>(tb + (koff0 ^ (uint32_t)(c << 5)) + 32 * kb * RB);
+    };
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) s[kb] = f32x16{};
-    // The K fragments of d chunk c + 1 are read while chunk c multiplies (two chunks in
-    // registers), and the schedule below keeps the reads two chunks ahead of the MFMAs: left
-    // to itself the compiler reads one fragment at a time into one register quad and waits
-    // for each read before its MFMA.
-    bf16x8 a[2][4];
+    for (int kb = 0; kb < 2; ++kb) a[0][kb] = kfrag(0, kb);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) a[0][kb] = *reinterpret_cast<const bf16x8*>(smem + koff[0] + 32 * kb * RB);
+    for (int kb = 0; kb < 2; ++kb) a[1][kb] = kfrag(1, kb);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      if (c + 1 < NC) {
+      if (c + 2 < NC) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          a[(c + 1) & 1][kb] = *reinterpret_cast<const bf16x8*>(smem + koff[c + 1] + 32 * kb * RB);
+        for (int kb = 0; kb < 2; ++kb) a[(c + 2) % 3][kb] = kfrag(c + 2, kb);
       }
+      if (c < NLD) copy16_async(kbase, ko[c], nb + row0 * RB + c * 1024);
+      else if (c < 2 * NLD) copy16_async(vbase, ko[c - NLD], nb + SUB_B + row0 * RB + (c - NLD) * 1024);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c & 1][kb], qf[c], s[kb], 0, 0, 0);
+      for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c % 3][kb], qf[c], s[kb], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads of chunks 0 and 1
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the fragments of chunks 0 and 1
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                     // the MFMAs of chunk c
-      if (c + 2 < NC) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // the reads of chunk c + 2
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                  // the MFMAs of chunk c
+      if (c + 2 < NC) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the fragments of chunk c + 2
     }
     // accumulator j of key block kb holds key 32*kb + 16*(j/8) + 8*half + j%8
-    if (nvalid < kTile) {
+    if (nvalid < kSub) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
           if (32 * kb + 16 * (j / 8) + 8 * half + (j % 8) >= nvalid) s[kb][j] = -INFINITY;
     }
     float mx = s[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
     const float m_new = fmaxf(m_run, max_xor32(mx));
@@ -254,10 +256,10 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
       for (int i = 0; i < ND; ++i) o[i] *= alpha;
     }
     const float mc = m_run * c2;
-    bf16x8 pb[8];  // P^T chunk t holds keys 16t + 8*half + e
+    bf16x8 pb[4];  // P^T chunk t holds keys 16t + 8*half + e
     float lsum = l_run;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         f32x8 pv;
@@ -271,28 +273,62 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
         lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk, pk, 6, 7), ones, lsum, false);
       }
     l_run = lsum;
+    auto vfrag = [&](int t, int db) {
+      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((UF_LDS i16x4*)(tb + voff[db][0] + 16 * t * RB));
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((UF_LDS i16x4*)(tb + voff[db][1] + 16 * t * RB));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 va[2][ND];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      bf16x8 a[ND];
+    for (int db = 0; db < ND; ++db) va[0][db] = vfrag(0, db);
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((UF_LDS i16x4*)(smem + voff[db][0] + 16 * t * RB));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((UF_LDS i16x4*)(smem + voff[db][1] + 16 * t * RB));
-        a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int t = 0; t < 4; ++t) {
+      if (t + 1 < 4) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db) va[(t + 1) & 1][db] = vfrag(t + 1, db);
       }
 #pragma unroll
-      for (int db = 0; db < ND; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], pb[t], o[db], 0, 0, 0);
+      for (int db = 0; db < ND; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t & 1][db], pb[t], o[db], 0, 0, 0);
     }
   };
 
-  // ---- main loop: the other work-group on this CU computes while this one loads
-  bool own;
-  for (int kt = tiles.next(lane, own); kt >= 0; kt = tiles.next(lane, own)) {
-    issue(kt);
+  // ---- main loop over sub-tiles (kept tile kt gives sub-tiles 2 kt and 2 kt + 1; the second is
+  // skipped when it holds no visible key).  Sub-tile j sits in buffer j % 2.
+  bool own_t = false, own_n = false;
+  int kt = tiles.next(lane, own_t);
+  int h = 0;
+  uint32_t ko[NLD];
+  copy_offsets(kt >= 0 ? kt * kTile : -1, ko);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) copy16_async(kbase, ko[i], smem + row0 * RB + i * 1024);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) copy16_async(vbase, ko[i], smem + SUB_B + row0 * RB + i * 1024);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int j = 0; kt >= 0; ++j) {
+    // the next sub-tile
+    int nkt = kt, nh = 1;
+    own_n = own_t;
+    if (h == 1 || kt * kTile + kSub >= p.n_k) {
+      nkt = tiles.next(lane, own_n);
+      nh = 0;
+    }
+    copy_offsets(nkt >= 0 ? nkt * kTile + nh * kSub : -1, ko);
+    const char* tb = smem + (j & 1) * 2 * SUB_B;
+    char* nb = smem + ((j + 1) & 1) * 2 * SUB_B;
+    if (own_t) {
+      compute(min(kSub, p.n_k - (kt * kTile + h * kSub)), tb, nb, ko);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) copy16_async(kbase, ko[i], nb + row0 * RB + i * 1024);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) copy16_async(vbase, ko[i], nb + SUB_B + row0 * RB + i * 1024);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // the tile is in LDS for every wave
-    if (own) compute(min(kTile, p.n_k - kt * kTile));
-    __syncthreads();  // every wave is done with the tile before the next one lands
+    __syncthreads();  // sub-tile j + 1 is in LDS and every wave is done with sub-tile j
+    kt = nkt;
+    h = nh;
+    own_t = own_n;
   }
 
   // ---- epilogue.  O^T accumulator j of d block db holds d = 32*db + 8*(j/4) + 4*half + j%4.
