@@ -49,9 +49,9 @@ def test_block_order_storage_bit_exact():
     cache.close()
 
 
-def run_block_stream(cfg, fp8=False, scales=(0.02, 0.015, 0.02)):
+def run_block_stream(cfg, fp8=False, scales=(0.02, 0.015, 0.02), **cache_kw):
     F = cfg.frames_per_step
-    kw = dict(block_grid=cfg.grid)
+    kw = dict(block_grid=cfg.grid, **cache_kw)
     if fp8:
         kw.update(kv_dtype=uf.UF_FP8_E4M3, q_scale=scales[0], k_scale=scales[1], v_scale=scales[2])
     cache = KVCache(cfg.n_kv_heads, cfg.head_dim, cfg.tokens_per_frame, cfg.window_frames, cfg.anchor_frames, **kw)
@@ -106,6 +106,13 @@ BLOCK_CASES = [
 @pytest.mark.parametrize("cfg", BLOCK_CASES, ids=lambda c: c.name)
 def test_block_order_attention(cfg):
     run_block_stream(cfg)
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+def test_block_order_split_key_ranges(splits):
+    """Block order with the key range forced into parts (attention partials, then the combine
+    kernel, which writes the raster-order output rows)."""
+    run_block_stream(Workload(76, "b-split", "bf16", 4, 2, 128, (10, 20), 2, 4, 2, 4, 50), splits=splits)
 
 
 def test_block_order_fp8_attention():

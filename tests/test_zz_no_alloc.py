@@ -84,3 +84,23 @@ def test_forced_splits_beyond_the_scratch_are_refused():
         bare.attn_step_static(q, out)
     bare.close()
     full.close()
+
+
+def test_static_scratch_fp8_cache():
+    """An E4M3 cache through the static entry point: bit for bit the workspace entry point's
+    result (which the FP8 tests hold to the oracle within the derived E4M3 bound), forced to
+    3 key-range parts, then a smaller call."""
+    cfg = Workload(83, "no-alloc-fp8", "bf16", 12, 3, 128, (30, 40), 1, 3, 0, 3, None)
+    kw = dict(kv_dtype=uf.UF_FP8_E4M3, q_scale=0.02, k_scale=0.015, v_scale=0.02, splits=3)
+    bare, full, _, qb = _stream(cfg, 3, **kw)
+    for n_q in (1200, 300):
+        q = to_dev(qb[:n_q])
+        a = torch.full_like(q, 3.0)
+        b = torch.full_like(q, -3.0)
+        print(f"fp8 static: {n_q} queries", flush=True)
+        bare.attn_step_static(q, a)
+        full.attn_step(q, b)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{n_q} queries: static scratch differs"
+    bare.close()
+    full.close()
