@@ -526,3 +526,16 @@ def test_largest_head_storage_is_accepted():
     hh = ctypes.c_void_p()
     assert LIB.uf_kvcache_create(ctypes.byref(dd), ctypes.byref(hh)) == uf.UF_OK, uf.uf_last_error()
     uf.uf_kvcache_destroy(hh.value)
+
+
+def test_header_compiles_as_c(tmp_path):
+    """include/uf.h is a C header: the plain-C program that drives the ABI compiles and links
+    against the library with -Werror (it runs in the GPU tests)."""
+    import shutil
+    import subprocess
+    from windowed_attention_amd import build as b
+    if not shutil.which("gcc"):
+        pytest.skip("needs gcc")
+    res = subprocess.run(b.c_check_command(str(tmp_path / "uf_c_check"), extra=("-Werror",)),
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stdout + res.stderr

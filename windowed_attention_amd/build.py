@@ -64,7 +64,33 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
     os.replace(tmp, LIB)
+    build_c_check(verbose)
     return LIB
+
+
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "uf_c_check.c")
+C_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi", "uf_c_check")
+
+
+def c_check_command(out: str, extra=()) -> list:
+    """gcc command line for the plain-C program that drives the C ABI (tests/c_abi): the header
+    must compile as C, and the program links the library and the HIP runtime only."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    return ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", *extra, "-D__HIP_PLATFORM_AMD__",
+            "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"), C_CHECK_SRC, "-o", out,
+            "-L", PKG, "-luf", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+            "-Wl,-rpath,$ORIGIN/../../windowed_attention_amd", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+
+
+def build_c_check(verbose: bool = False) -> str:
+    """Build the plain-C check of the ABI next to its source."""
+    cmd = c_check_command(C_CHECK_BIN)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"building the C check failed:\n{res.stdout}{res.stderr}")
+    return C_CHECK_BIN
 
 
 if __name__ == "__main__":
