@@ -103,12 +103,16 @@ __device__ __forceinline__ int swz(int row) {
     return ((r & 1) ? 2 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 3 : 0);
 }
 
-constexpr int kAttnThreads = 256;  // 4 waves; two work-groups per CU
+constexpr int kAttnThreads = 256;  // 4 waves
+// Work-groups per CU the register allocation is held to: two at d = 128 (LDS 64 KB each); four
+// at d = 64 (LDS 32 KB, 128 registers per wave: decoder-XL and refine-XL +3% over three).
+template <int D>
+constexpr int attn_wgs_per_cu() { return D == 64 ? 4 : 2; }
 
 constexpr int kSub = 64;  // keys per sub-tile: two per key tile
 
 template <int D>
-__global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnParams p) {
+__global__ void __launch_bounds__(kAttnThreads, attn_wgs_per_cu<D>()) attn_kernel(AttnParams p) {
   constexpr int NC = D / 16;            // 16-wide d chunks of the S^T mfma
   constexpr int ND = D / 32;            // 32-row d blocks of O^T
   constexpr int CPR = D / 8;            // 16-byte chunks per LDS row
