@@ -539,3 +539,49 @@ def test_header_compiles_as_c(tmp_path):
     res = subprocess.run(b.c_check_command(str(tmp_path / "uf_c_check"), extra=("-Werror",)),
                          capture_output=True, text=True)
     assert res.returncode == 0, res.stdout + res.stderr
+
+
+from hypothesis import HealthCheck, given, settings, strategies as hst  # noqa: E402
+
+_OPS = hst.lists(hst.tuples(hst.sampled_from(["append", "overwrite", "crop", "reset"]), hst.integers(0, 9)),
+                 min_size=1, max_size=40)
+
+
+@settings(max_examples=200, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(L=hst.integers(1, 40), W=hst.integers(1, 6), A=hst.integers(0, 4), ops=_OPS)
+def test_window_bookkeeping_random_sequences(L, W, A, ops):
+    """Random sequences of appends (some beyond the ring's capacity), overwrites (some of the
+    wrong size), crops (some out of range) and resets.  Each call succeeds exactly when
+    include/uf.h says it may, a refused call leaves the window as it was, and after every call
+    the window and the storage row of every visible key equal the independent ring model's."""
+    st, h = create(H=1, d=64, L=L, W=W, A=A)
+    assert st == uf.UF_OK
+    model, active = RingModel(1, 64, L, W, A), W
+    try:
+        for op, n in ops:
+            before = _window(h)
+            if op == "append":
+                ok = max(0, n - max(0, A - model.count)) <= W
+                got = LIB.uf_kvcache_append(h, None, None, n, uf.UF_APPEND_COMMIT_ONLY, None)
+                if ok and n > 0:
+                    model.append(n)
+            elif op == "overwrite":
+                ok = model.last > 0 and n == model.last
+                got = LIB.uf_kvcache_append(h, None, None, n, uf.UF_APPEND_OVERWRITE_NEWEST | uf.UF_APPEND_COMMIT_ONLY,
+                                            None)
+            elif op == "crop":
+                ok = 1 <= n <= W
+                got = LIB.uf_kvcache_set_window(h, n)
+                if ok:
+                    active = n
+            else:
+                ok = True
+                got = LIB.uf_kvcache_reset(h)
+                model, active = RingModel(1, 64, L, W, A), W
+            assert (got == uf.UF_OK) == ok, (op, n, got, uf.uf_last_error())
+            if not ok:
+                assert _window(h) == before, (op, n)
+            _check_window(h, model, W, A, L, active)
+            assert _window(h)["active_frames"] == active
+    finally:
+        uf.uf_kvcache_destroy(h)
