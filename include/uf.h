@@ -110,7 +110,12 @@ typedef struct uf_tensor {
  * appended.  UF_FP8_E4M3 stores one byte per element with static scales
  * (FlashDecoder review, inference optimisations: statically calibrated FP8):
  * k and v are stored as E4M3(x / k_scale) and E4M3(x / v_scale), and every
- * step quantizes its queries as E4M3(q / q_scale); E4M3() rounds to nearest
+ * step quantizes its queries as E4M3(q / q_scale'), where q_scale' is q_scale
+ * rounded up, by less than a factor of two, so that
+ * log2(e)/sqrt(head_dim) * q_scale' * k_scale is a power of two 2^e (computed in
+ * double from the float scales: e = ceil(log2 of that product with q_scale),
+ * q_scale' = float(2^e / (log2(e)/sqrt(head_dim) * k_scale)); e must lie in
+ * -120..120); E4M3() rounds to nearest
  * (ties to even; the quotient is x times the reciprocal of the float scale,
  * computed in double and rounded to float, the product rounded to float) and
  * saturates at +-448; a value that rounds to zero keeps its sign.  The step then attends over the dequantized

@@ -11,6 +11,10 @@ attention path this is read as:
     rounding to the nearest representable value (ties to the even code, a
     value that rounds to zero keeping its sign) and saturating at +-448; the
     value is then code * scale.
+  * q's scale for attention is the caller's q_scale rounded up, by less than a
+    factor of two, so that log2(e)/sqrt(d) * q_scale' * k_scale is a power of two
+    (attention_q_scale; the pages fix no rule for it: a static calibration picks
+    a scale, and this choice only moves the top of q's range up, never down).
   * The attention itself is the plain definition (oracle.attention.attend)
     applied to those dequantized values in float64.
 
@@ -20,6 +24,8 @@ subnormals m/8 * 2^-6; no infinities; S.1111.111 is NaN, so the largest
 finite magnitude is 1.75 * 2^8 = 448.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -74,3 +80,20 @@ def quantize(x: np.ndarray, scale: float) -> np.ndarray:
 def dequantize(codes: np.ndarray, scale: float) -> np.ndarray:
     """Values code * scale in float64, the scale taken as a float32."""
     return e4m3_decode(codes) * float(np.float32(scale))
+
+
+def attention_q_scale(q_scale: float, k_scale: float, head_dim: int) -> float:
+    """The scale q is quantized with for attention (float32, returned as a Python float).
+
+    With c = log2(e)/sqrt(head_dim) and the float32 scales, x = c * q_scale * k_scale; the
+    exponent e = ceil(log2 x) (x = f 2^e' with f in [0.5, 1) from frexp: e = e' - 1 when f is
+    exactly 0.5, else e'); the result is float32(2^e / (c * k_scale)), i.e. the smallest
+    q_scale' >= q_scale (up to that rounding) with c * q_scale' * k_scale a power of two.
+    Every step is taken in float64 from the float32 scales."""
+    c = 1.4426950408889634 / math.sqrt(head_dim)
+    ks = float(np.float32(k_scale))
+    x = c * float(np.float32(q_scale)) * ks
+    f, e = math.frexp(x)
+    if f == 0.5:
+        e -= 1
+    return float(np.float32(math.ldexp(1.0, e) / (c * ks)))

@@ -57,6 +57,7 @@ hipError_t launch_attention(const AttnParams& p, int, hipStream_t) {
 
 hipError_t launch_attention_fp8(const AttnFp8Params& p, int, hipStream_t) {
   check_attn(p.a);
+  require(p.q_e8m0 >= 7 && p.q_e8m0 <= 247 && p.q_inv_scale > 0.f && p.v_scale > 0.f, "fp8 attention scales");
   ++g_launches;
   return hipSuccess;
 }

@@ -64,7 +64,8 @@ def run_block_stream(cfg, fp8=False, scales=(0.02, 0.015, 0.02), **cache_kw):
         if fp8:
             k = f8.dequantize(f8.quantize(k, scales[1]), scales[1])
             v = f8.dequantize(f8.quantize(v, scales[2]), scales[2])
-            q = f8.dequantize(f8.quantize(q, scales[0]), scales[0])
+            qs = f8.attention_q_scale(scales[0], scales[1], cfg.head_dim)
+            q = f8.dequantize(f8.quantize(q, qs), qs)
         win.append(_perm(cfg, k), _perm(cfg, v), F)
         n_k = cache.window().n_keys
         mask_np = mask_d = None

@@ -105,7 +105,7 @@ def run_fp8_stream(cfg, check_steps=None, tiles=None, scales=SCALES, **cache_kw)
         sel_tiles = range(nqt) if tiles is None or tiles >= nqt else \
             sorted({0, nqt - 1, *np.random.default_rng(s).choice(np.arange(1, nqt - 1), tiles - 2, replace=False)})
         rows = np.concatenate([np.arange(t * TILE, min((t + 1) * TILE, cfg.q_tokens)) for t in sel_tiles])
-        qq = fp8_lut.round_trip_bits(qb, q_s)
+        qq = fp8_lut.round_trip_bits(qb, f8.attention_q_scale(q_s, k_s, cfg.head_dim))
         kk, vv = win.keys_values()
         ref = oracle_rows(qq, kk, vv, mask_np, rows)
         # the bound is row-wise: evaluate it on the same tile groups, each with its rows' ref

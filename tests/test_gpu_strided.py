@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import oracle.fp8 as f8
 from synth import TILE, Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
 from tests import fp8_lut
 from tests.fp8_bound import bound
@@ -63,7 +64,7 @@ def test_fused_qkv_and_strided_out(kind):
         got = bf16_bits_to_f32(w[:, 1:1 + cfg.n_q_heads]).astype(np.float64)
         kk, vv = win.keys_values()
         if kind == "fp8":
-            qq = fp8_lut.round_trip_bits(qb, SCALES[0])
+            qq = fp8_lut.round_trip_bits(qb, f8.attention_q_scale(SCALES[0], SCALES[1], cfg.head_dim))
             ref = oracle.attend(qq, kk, vv, mask_np)
             ratio = float((np.abs(got - ref) / bound(qq, kk, vv, ref, mask_np, np.arange(cfg.q_tokens))).max())
             print(f"  largest error / E4M3 bound = {ratio:.3f}", flush=True)

@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle
+import oracle.fp8 as f8
 import oracle.blocks as ob
 from synth import Workload, bf16_bits_to_f32, draw_step_tensors, make_block_mask
 from tests import fp8_lut
@@ -76,7 +77,7 @@ def test_overwrite_and_crop(kind):
         torch.cuda.synchronize()
         got = f32_of(out)
         if kind == "fp8":
-            qq = fp8_lut.round_trip_bits(qb, SCALES[0])
+            qq = fp8_lut.round_trip_bits(qb, f8.attention_q_scale(SCALES[0], SCALES[1], cfg.head_dim))
             rows = np.arange(cfg.q_tokens)
             ref = oracle.attend(qq, kk, vv, mask_np)
             ratio = float((np.abs(got.astype(np.float64) - ref) / _bound(qq, kk, vv, ref, mask_np, rows)).max())

@@ -312,6 +312,7 @@ def test_fp8_cache_description():
         (fp8_desc(scales=(1.0, 1.0, float("inf"))), uf.UF_ERR_INVALID_ARG),
         (fp8_desc(scales=(1.0, 1.0, float("nan"))), uf.UF_ERR_INVALID_ARG),
         (fp8_desc(scales=(1e-45, 1.0, 1.0)), uf.UF_ERR_INVALID_ARG),   # reciprocal overflows float
+        (fp8_desc(scales=(1e-30, 1e-30, 1.0)), uf.UF_ERR_INVALID_ARG),  # q k scale product beyond E8M0
     ]
     for d, want in bad:
         h = ctypes.c_void_p()

@@ -75,7 +75,31 @@ def check_static_quantization():
     assert f8.dequantize(np.array([0x4C]), 0.5)[0] == 3.0
 
 
-ALL = [check_golden, check_order_and_round_trip, check_brute_force, check_static_quantization]
+def check_attention_q_scale():
+    """q's scale for attention: never below q_scale, below twice it, and log2(e)/sqrt(d) times it
+    times k_scale a power of two, the smallest such (exponent = ceil of the log2, by math.log2);
+    and one value worked by hand: d = 128, q_scale 0.02, k_scale 0.015 give
+    log2(log2(e)/sqrt(128) * 0.02 * 0.015) = log2(3.8255e-5) = -14.67, exponent -14, scale
+    2^-14 sqrt(128) / (log2(e) 0.015) = 0.0319094."""
+    import math
+    assert abs(f8.attention_q_scale(0.02, 0.015, 128) / 0.0319094 - 1.0) < 2e-6
+    rng = np.random.default_rng(7)
+    for _ in range(300):
+        d = int(rng.choice([64, 128]))
+        qs = float(np.float32(np.exp(rng.uniform(-9, 3))))
+        ks = float(np.float32(np.exp(rng.uniform(-9, 3))))
+        r = f8.attention_q_scale(qs, ks, d)
+        assert qs * (1 - 2.0 ** -22) <= r < 2 * qs * (1 + 2.0 ** -22), (qs, ks, d, r)
+        c = math.log2(math.e) / math.sqrt(d)
+        lg = math.log2(c * r * ks)
+        assert abs(lg - round(lg)) < 1e-6, (qs, ks, d, lg)
+        want = math.log2(c * qs * ks)
+        if abs(want - round(want)) > 1e-9:
+            assert round(lg) == math.ceil(want), (qs, ks, d, lg, want)
+
+
+ALL = [check_golden, check_order_and_round_trip, check_brute_force, check_static_quantization,
+       check_attention_q_scale]
 
 
 @pytest.mark.parametrize("check", ALL, ids=lambda f: f.__name__)
@@ -113,7 +137,22 @@ def _decode_sub_spacing(codes):
     return np.where(((c >> 3) & 0xF) == 0, v / 2.0, v)
 
 
+ORIG_Q_SCALE = f8.attention_q_scale
+
+
+def _q_scale_floor(q_scale, k_scale, head_dim):
+    # rounds the exponent down instead of up
+    return ORIG_Q_SCALE(q_scale, k_scale, head_dim) / 2.0
+
+
+def _q_scale_no_sqrt(q_scale, k_scale, head_dim):
+    # softmax factor log2(e)/d instead of log2(e)/sqrt(d)
+    return ORIG_Q_SCALE(q_scale, k_scale, head_dim * head_dim)
+
+
 MUTANTS = {
+    "q_scale_exponent_floor": ("attention_q_scale", _q_scale_floor),
+    "q_scale_no_sqrt": ("attention_q_scale", _q_scale_no_sqrt),
     "decode_bias_8": ("e4m3_decode", _decode_bias8),
     "encode_ties_away": ("e4m3_encode", _encode_ties_away),
     "encode_no_saturation": ("e4m3_encode", _encode_no_saturation),

@@ -44,6 +44,8 @@ uf_status hip_fail(hipError_t e, const char* what) {
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;
 constexpr int kMaxSplits = 16;
 
+float fp8_attention_q_scale(const uf_kvcache_desc& d, int* e_out);
+
 uf_status check_desc(const uf_kvcache_desc* d) {
   if (!d) return fail(UF_ERR_INVALID_ARG, "desc is NULL");
   if (d->n_kv_heads < 1) return fail(UF_ERR_SHAPE, "n_kv_heads must be >= 1 (got %d)", d->n_kv_heads);
@@ -74,12 +76,31 @@ uf_status check_desc(const uf_kvcache_desc* d) {
     for (float x : sc)
       if (!(x > 0.f) || !isfinite(x) || !isfinite(1.0f / x))
         return fail(UF_ERR_INVALID_ARG, "FP8 scales must be positive, finite and invertible");
+    int e = 0;
+    const float qs = fp8_attention_q_scale(*d, &e);
+    if (e < -120 || e > 120 || !(qs > 0.f) || !isfinite(qs) || !isfinite(1.0f / qs))
+      return fail(UF_ERR_INVALID_ARG, "FP8 scales: log2(e)/sqrt(head_dim) q_scale k_scale = 2^%d is out of range", e);
   }
   return UF_OK;
 }
 
 int elem_bytes(const uf_kvcache_desc& d) { return d.kv_dtype == UF_FP8_E4M3 ? 1 : 2; }
 float inv_scale(float s) { return (float)(1.0 / (double)s); }
+
+// The scale an FP8 step quantizes q with: q_scale rounded up, by less than a factor of two, so
+// that the product of the softmax factor log2(e)/sqrt(d) and the two scales is a power of two
+// 2^e (e = ceil(log2(log2(e)/sqrt(d) q_scale k_scale))).  The kernel then applies 2^e as the
+// Q operand's E8M0 scale and gets the scores in log2 units with no multiply.  Computed in
+// double from the float scales and rounded to float.
+float fp8_attention_q_scale(const uf_kvcache_desc& d, int* e_out) {
+  const double c0 = 1.4426950408889634 / sqrt((double)d.head_dim);
+  const double x = c0 * (double)d.q_scale * (double)d.k_scale;
+  int e = 0;
+  const double f = frexp(x, &e);  // x = f 2^e, f in [0.5, 1)
+  if (f == 0.5) e -= 1;           // x is a power of two already
+  *e_out = e;
+  return (float)(ldexp(1.0, e) / (c0 * (double)d.k_scale));
+}
 
 int64_t rows_per_head(const uf_kvcache_desc& d) {
   return ((int64_t)d.anchor_frames + d.window_frames) * d.tokens_per_frame;
@@ -498,8 +519,9 @@ uf_status attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mask* 
   if (d.kv_dtype == UF_FP8_E4M3) {
     uf::AttnFp8Params f;
     f.a = p;
-    f.a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d.head_dim) * (double)d.q_scale * (double)d.k_scale);
-    f.q_inv_scale = inv_scale(d.q_scale);
+    int q_exp = 0;
+    f.q_inv_scale = inv_scale(fp8_attention_q_scale(d, &q_exp));
+    f.q_e8m0 = 127 + q_exp;
     f.v_scale = d.v_scale;
     e = uf::launch_attention_fp8(f, d.head_dim, (hipStream_t)stream);
   } else {

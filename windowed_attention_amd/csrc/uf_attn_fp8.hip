@@ -56,6 +56,16 @@ __device__ inline int pack4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
+// four floats divided by the power of two of `scale` (its exponent; v_cvt_scalef32) -> one
+// dword of E4M3 codes, low byte first
+__device__ inline int pack4_scaled(float a, float b, float c, float d, float scale) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  s16x2 w = __builtin_bit_cast(s16x2, __float_as_int(a));  // both halves are overwritten
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, scale, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, scale, true);
+  return __builtin_bit_cast(int, w);
+}
+
 // eight bf16 (one 16-byte load) times s -> two dwords of E4M3 codes
 __device__ inline void quant8(const uint4& v, float s, int& w0, int& w1) {
   w0 = pack4(sat(bf16_lo(v.x) * s), sat(bf16_hi(v.x) * s), sat(bf16_lo(v.y) * s), sat(bf16_hi(v.y) * s));
@@ -161,7 +171,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
   for (int i = 0; i < ND; ++i) o[i] = f32x16{};
   f32x16 lacc = f32x16{};    // every element: this lane's query's sum of rounded probabilities
   float m_run = -INFINITY;   // reference max (raw score units) of this lane's query
-  const float c2 = p.scale_log2;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) + (int64_t)kvh * p.kv_head_stride;
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) + (int64_t)kvh * p.kv_head_stride;
   KeyTiles tiles(p, it);  // the kept key tiles, ascending
@@ -223,6 +232,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
   auto mfma8 = [](const i32x8& a, const i32x8& b, const f32x16& c) -> f32x16 {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
   };
+  // S = K Q^T with the power of two 2^E of q's scale applied to the Q operand (E8M0 scale
+  // 127 + E): the accumulators then hold the scores in log2 units exactly, with no multiply
+  const int q_e8m0 = pp.q_e8m0;
+  auto mfma8q = [q_e8m0](const i32x8& a, const i32x8& b, const f32x16& c) -> f32x16 {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, q_e8m0);
+  };
 
   auto compute = [&](int nvalid, int buf) {
     const char* tb = smem + buf * BUF_B;
@@ -245,7 +260,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
 #pragma unroll
     for (int m = 0; m < NS; ++m) {
       if (m + 2 < NS) ka[(m + 2) % 3] = kfrag(m + 2);
-      s[m % 4] = mfma8(ka[m % 3], qf[m / 4], s[m % 4]);
+      s[m % 4] = mfma8q(ka[m % 3], qf[m / 4], s[m % 4]);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the fragments of MFMAs 0 and 1
 #pragma unroll
@@ -266,29 +281,45 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+    // Lazy rescaling against an integer reference point m_run (log2 units): it moves, to the
+    // floor of the running max, only when the max has grown by more than 8, so P stays below
+    // 2^8 (E4M3 holds 448) and every rescaling factor is an exact power of two.
     const float m_new = fmaxf(m_run, max_xor32(mx));
-    const bool need = (m_new - m_run) * c2 > 8.f;  // lazy rescaling: P stays <= 2^8
+    const bool need = m_new - m_run > 8.f;
     if (__ballot(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c2) : 1.f;
-      if (need) m_run = m_new;
+      const float ref = need ? floorf(m_new) : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - ref);  // 0 for the first tile (-inf)
+      m_run = ref;
       lacc *= alpha;
 #pragma unroll
       for (int i = 0; i < ND; ++i) o[i] *= alpha;
     }
-    const float mc = m_run * c2;
+    // P = E4M3(2^(s - m_run)).  While |m_run| <= 96 the conversion divides by 2^m_run itself
+    // (v_cvt_scalef32, exact on the fp32 value 2^s: s <= m_run + 8 cannot overflow, and where 2^s
+    // leaves the normal range the code is 0 either way), so no subtraction per score is needed.
+    const bool scaled = __ballot(!(fabsf(m_run) <= 96.f)) == 0;
+    const float ref_scale = __int_as_float(((int)m_run + 127) << 23);  // 2^m_run when scaled
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       // P^T (B operand) of keys 64t .. 64t + 63: byte 8r + k of lane half h is key
       // 64t + 16r + 8h + k, i.e. dword w packs accumulators 4(w & 3) .. +3 of key block 2t + w / 4
       i32x8 pf;
+      if (scaled) {
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const f32x16& blk = s[2 * t + (w >> 2)];
-        const int j = 4 * (w & 3);
-        pf[w] = pack4(__builtin_amdgcn_exp2f(__builtin_fmaf(blk[j], c2, -mc)),
-                      __builtin_amdgcn_exp2f(__builtin_fmaf(blk[j + 1], c2, -mc)),
-                      __builtin_amdgcn_exp2f(__builtin_fmaf(blk[j + 2], c2, -mc)),
-                      __builtin_amdgcn_exp2f(__builtin_fmaf(blk[j + 3], c2, -mc)));
+        for (int w = 0; w < 8; ++w) {
+          const f32x16& blk = s[2 * t + (w >> 2)];
+          const int j = 4 * (w & 3);
+          pf[w] = pack4_scaled(__builtin_amdgcn_exp2f(blk[j]), __builtin_amdgcn_exp2f(blk[j + 1]),
+                               __builtin_amdgcn_exp2f(blk[j + 2]), __builtin_amdgcn_exp2f(blk[j + 3]), ref_scale);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const f32x16& blk = s[2 * t + (w >> 2)];
+          const int j = 4 * (w & 3);
+          pf[w] = pack4(__builtin_amdgcn_exp2f(blk[j] - m_run), __builtin_amdgcn_exp2f(blk[j + 1] - m_run),
+                        __builtin_amdgcn_exp2f(blk[j + 2] - m_run), __builtin_amdgcn_exp2f(blk[j + 3] - m_run));
+        }
       }
       lacc = mfma8(ones, pf, lacc);
       // V^T fragments one d block ahead of their MFMA (the same ordering trick as for K)
@@ -366,7 +397,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
         *reinterpret_cast<f32x4*>(wo + 32 * db + 8 * g + 4 * half) = x;
       }
     if (half == 0) {
-      p.ws_ml[2 * row] = m_run * c2;
+      p.ws_ml[2 * row] = m_run;  // log2 units; -inf when this split saw no key
       p.ws_ml[2 * row + 1] = l;
     }
   }

@@ -69,6 +69,7 @@ struct AppendFp8Params {
 struct AttnFp8Params {
   AttnParams a;                // k, v point to uint8 storage; scale_log2 = log2(e) q_scale k_scale / sqrt(d)
   float q_inv_scale;           // q is quantized as E4M3(q * q_inv_scale)
+  int q_e8m0;                  // 127 + E: the scores in log2 units are 2^E sum_c q8_c k8_c
   float v_scale;               // O = v_scale * sum_j P_j V8_j / sum_j P_j
 };
 
