@@ -77,14 +77,14 @@ def _same_codes(storage, want, what):
     assert len(bad) == 0, f"{what}: {len(bad)} codes differ"
 
 
-def run_fp8_stream(cfg, check_steps=None, tiles=None, scales=SCALES, **cache_kw):
+def run_fp8_stream(cfg, check_steps=None, tiles=None, scales=SCALES, scale_q=1.0, **cache_kw):
     q_s, k_s, v_s = scales
     cache = _fp8_cache(cfg, scales, **cache_kw)
     win = oracle.FrameListWindow(cfg.tokens_per_frame, cfg.window_frames, cfg.anchor_frames)
     check_steps = range(cfg.steps) if check_steps is None else check_steps
     worst = 0.0
     for s in range(cfg.steps):
-        qb, kb, vb = draw_step_tensors(cfg, s)
+        qb, kb, vb = draw_step_tensors(cfg, s, scale_q)
         q_d = to_dev(qb)
         print(f"{cfg.name} step {s}: fp8 append + attend", flush=True)
         cache.append(to_dev(kb), to_dev(vb), cfg.frames_per_step)
@@ -167,3 +167,13 @@ def test_fp8_decoder_shape():
 def test_fp8_other_scales():
     # a coarser q scale and a finer v scale
     run_fp8_stream(Workload(65, "f8-scales", "bf16", 2, 2, 128, (8, 25), 1, 3, 0, 4, None), scales=(0.05, 0.01, 0.005))
+
+
+@pytest.mark.parametrize("scale_q", [12.0, 120.0])
+def test_fp8_large_scores(scale_q):
+    """Scores of tens to hundreds in log2 units (q scaled up; q's scale 1.0 keeps it in range).
+    While the reference point stays within +-96 the kernel converts P with the scaled
+    conversion; beyond, with a subtraction per score.  q x 12 stays mostly within, q x 120
+    goes beyond on almost every row."""
+    cfg = Workload(67, "f8-large", "bf16", 2, 2, 128, (8, 25), 1, 3, 0, 3, None)
+    run_fp8_stream(cfg, scales=(1.0, 0.015, 0.02), scale_q=scale_q)
