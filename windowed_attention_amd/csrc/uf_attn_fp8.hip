@@ -5,10 +5,12 @@
 // calibrated FP8 for the matrix products): q, k and v are each quantized with one static
 // scale, code = E4M3(x / scale) rounded to nearest even and saturated at +-448.  The step
 // then computes softmax(Q K^T / sqrt(d)) V on the dequantized values:
-//   S^T = K8 . Q8^T       mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulate),
-//                         the score scale q_scale * k_scale * log2(e) / sqrt(d) folded into
-//                         the exponent as in the bf16 kernel
-//   P                     fp32 online softmax (lazy rescaling), then E4M3 (P <= 2^8 < 448)
+//   S^T = K8 . Q8^T       mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulate);
+//                         q is quantized with its scale rounded up so that
+//                         log2(e) / sqrt(d) * q_scale * k_scale is a power of two 2^e, and 2^e
+//                         is the Q operand's E8M0 scale: the scores come out in log2 units
+//   P                     fp32 online softmax (lazy rescaling against an integer reference
+//                         point m), E4M3(2^s / 2^m) from the scaled conversion (P <= 2^8 < 448)
 //   O^T += V8^T . P8^T    the same mfma; V^T fragments come from the row-major V tile with
 //                         the gfx950 LDS transpose read of bytes (ds_read_b64_tr_b8)
 //   l                     one more mfma per 64 keys with an all-ones A operand, so the row
@@ -298,7 +300,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnFp8Params pp)
     // (v_cvt_scalef32, exact on the fp32 value 2^s: s <= m_run + 8 cannot overflow, and where 2^s
     // leaves the normal range the code is 0 either way), so no subtraction per score is needed.
     const bool scaled = __ballot(!(fabsf(m_run) <= 96.f)) == 0;
-    const float ref_scale = __int_as_float(((int)m_run + 127) << 23);  // 2^m_run when scaled
+    // 2^m_run (m_run clamped to the range the scaled path is taken in, so that the conversion
+    // to an integer is defined whatever m_run holds)
+    const float ref_scale = __int_as_float(((int)fminf(fmaxf(m_run, -96.f), 96.f) + 127) << 23);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       // P^T (B operand) of keys 64t .. 64t + 63: byte 8r + k of lane half h is key
