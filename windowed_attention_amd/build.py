@@ -15,7 +15,11 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libuf.so")
 ARCH = "gfx950"
 
-SOURCES = ["uf_api.cpp", "uf_kernels.hip", "uf_topk.hip", "uf_attn_fp8.hip"]
+SOURCES = ["uf_api.cpp", "uf_kernels.hip", "uf_attn_d128.hip", "uf_topk.hip", "uf_attn_fp8.hip"]
+# per-source options: the head_dim 128 attention kernel is scheduled with LLVM's "max-ilp"
+# strategy (1.3-2.3% faster on the 2K, 1K, 480P and decoder steps, measured side by side;
+# slower for the head_dim 64 and FP8 kernels, which keep the default)
+SOURCE_FLAGS = {"uf_attn_d128.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 # Packed fp32 VALU ops stay disabled on every device pass (-packed-fp32-ops).
 FLAGS = [
@@ -44,7 +48,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(obj_dir, exist_ok=True)
     for src in SOURCES:
         obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *FLAGS, *SOURCE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, capture_output=True, text=True)
