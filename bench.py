@@ -46,8 +46,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_traffic.md")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_kernel_mfma_counters.md")
 CSRC = os.path.join(ROOT, "windowed_attention_amd", "csrc")
 # every source compiled into the bf16 attention kernel (its schedule lives in the headers)
-KERNEL_SOURCES = ["uf_kernels.hip", "uf_attn_bf16.h", "uf_attn_d128.hip", "uf_attn_walk.h", "uf_device.h",
-                  "uf_internal.h"]
+KERNEL_SOURCES = ["uf_kernels.hip", "uf_attn_bf16.h", "uf_attn_d128.hip", "uf_attn_d64.hip", "uf_attn_walk.h",
+                  "uf_device.h", "uf_internal.h"]
 
 
 def kernel_sources_sha256():

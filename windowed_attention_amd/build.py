@@ -15,11 +15,14 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libuf.so")
 ARCH = "gfx950"
 
-SOURCES = ["uf_api.cpp", "uf_kernels.hip", "uf_attn_d128.hip", "uf_topk.hip", "uf_attn_fp8.hip"]
-# per-source options: the head_dim 128 attention kernel is scheduled with LLVM's "max-ilp"
-# strategy (1.3-2.3% faster on the 2K, 1K, 480P and decoder steps, measured side by side;
-# slower for the head_dim 64 and FP8 kernels, which keep the default)
-SOURCE_FLAGS = {"uf_attn_d128.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+SOURCES = ["uf_api.cpp", "uf_kernels.hip", "uf_attn_d128.hip", "uf_attn_d64.hip", "uf_topk.hip",
+           "uf_attn_fp8.hip"]
+# per-source options: LLVM's machine scheduling strategy for the two bf16 attention kernels,
+# each the fastest measured side by side ("max-ilp" at head_dim 128: 2K, 1K, 480P and decoder
+# steps 1.3-2.3% faster than the default; "iterative-ilp" at head_dim 64: decoder-XL and
+# refine-XL 1-2% faster); the FP8 kernel keeps the default, which is fastest for it
+SOURCE_FLAGS = {"uf_attn_d128.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+                "uf_attn_d64.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 # Packed fp32 VALU ops stay disabled on every device pass (-packed-fp32-ops).
 FLAGS = [

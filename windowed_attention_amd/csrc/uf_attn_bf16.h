@@ -1,9 +1,9 @@
 // The bf16 attention kernel of libuf (gfx950): chunk attention with bf16 MFMA, fp32 online
 // softmax and block-mask tile skipping over the rolling cache (FlashDecoder review, "Rolling
 // KV cache", Eq. 4; HiStream summary, innovation 2 for the anchor; Ultra Flash notes, key
-// design 3 for the block mask).  Included by uf_kernels.hip (head_dim 64, and the launch) and
-// uf_attn_d128.hip (head_dim 128, built with its own scheduling option): each has its own
-// copy of the template, with internal linkage.
+// design 3 for the block mask).  Included by uf_attn_d128.hip and uf_attn_d64.hip, each built
+// with its own scheduling option; each has its own copy of the template, with internal
+// linkage.
 #pragma once
 
 #include <hip/hip_runtime.h>

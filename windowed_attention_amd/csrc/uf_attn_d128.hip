@@ -1,7 +1,7 @@
 // The head_dim 128 instance of the bf16 attention kernel (uf_attn_bf16.h), in a translation
-// unit of its own: the library builds it with the LLVM AMDGPU scheduling strategy "max-ilp"
-// (the other kernels keep the default).  Measured side by side, that schedule runs the 2K,
-// 1K, 480P and decoder steps 1.3-2.3% faster; for the head_dim 64 and FP8 kernels it is slower.
+// unit of its own: the library builds it with the LLVM AMDGPU scheduling strategy "max-ilp".
+// Measured side by side, that schedule runs the 2K, 1K, 480P and decoder steps 1.3-2.3%
+// faster than the default; for the head_dim 64 and FP8 kernels it is slower.
 #include <hip/hip_runtime.h>
 
 #include "uf_attn_bf16.h"

@@ -117,6 +117,7 @@ hipError_t static_scratch(void** ptr);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_attention_d128(const AttnParams& p, hipStream_t stream);  // from launch_attention
+hipError_t launch_attention_d64(const AttnParams& p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_block_mask_topk(const TopkParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_append_fp8(const AppendFp8Params& p, hipStream_t stream);

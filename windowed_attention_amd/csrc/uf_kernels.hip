@@ -1,6 +1,6 @@
 // gfx950 kernels of libuf: rolling-cache append, the launch of the bf16 chunk attention
 // kernel (bf16 MFMA, fp32 online softmax, block-mask tile skipping; uf_attn_bf16.h, its
-// head_dim 128 instance in uf_attn_d128.hip) and the split-KV combine.
+// instances in uf_attn_d128.hip and uf_attn_d64.hip) and the split-KV combine.
 //
 // The attention operation is softmax(Q K^T / sqrt(d)) V over the cache's
 // visible keys (FlashDecoder review, "Rolling KV cache", Eq. 4; HiStream
@@ -11,13 +11,16 @@
 
 #include <mutex>
 
-#include "uf_attn_bf16.h"
 #include "uf_attn_walk.h"
 #include "uf_device.h"
 #include "uf_internal.h"
 
 namespace uf {
 namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;   // 4 waves of 64
 // ---------------------------------------------------------------------------
@@ -124,10 +127,7 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) return launch_attention_d128(p, stream);  // uf_attn_d128.hip
-  const int items = p.n_qblk * p.n_hgrp * p.splits;
-  hipLaunchKernelGGL(attn_kernel<64>, dim3(items), dim3(kAttnThreads), 0, stream, p);
-  return hipGetLastError();
+  return head_dim == 128 ? launch_attention_d128(p, stream) : launch_attention_d64(p, stream);
 }
 
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream) {
