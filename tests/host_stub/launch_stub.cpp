@@ -10,6 +10,7 @@
 
 namespace {
 int g_launches = 0;
+int g_last_splits = 0, g_last_split_tile = 0;
 
 void require(bool ok, const char* what) {
   if (!ok) {
@@ -20,6 +21,9 @@ void require(bool ok, const char* what) {
 }  // namespace
 
 extern "C" int uf_stub_launch_count(void) { return g_launches; }
+// key-range parts and body tiles of the last attention launch
+extern "C" int uf_stub_last_splits(void) { return g_last_splits; }
+extern "C" int uf_stub_last_split_tile(void) { return g_last_split_tile; }
 
 namespace uf {
 
@@ -47,6 +51,9 @@ static void check_attn(const AttnParams& p) {
   require(p.n_qblk == (p.n_q + 128 / p.heads_per_wg - 1) / (128 / p.heads_per_wg), "query blocks");
   require(p.anchor_keys >= 0 && p.anchor_keys <= p.n_k && p.ring_rot >= 0 && p.ring_rot < p.ring_cap, "window");
   require(p.n_k - p.anchor_keys <= p.ring_cap, "ring keys");
+  require(p.split_tile == 0 || (p.splits == 2 && p.split_tile > 0 && p.split_tile < p.n_kb), "uneven split");
+  g_last_splits = p.splits;
+  g_last_split_tile = p.split_tile;
 }
 
 hipError_t launch_attention(const AttnParams& p, int, hipStream_t) {

@@ -146,6 +146,12 @@ def test_fp8_per_head_masks_shared_tiles(hpw):
 
 
 @pytest.mark.timeout(600)
+def test_fp8_uneven_split():
+    # 320 dense work items: cut into bodies and tails of the key range, then combined
+    run_fp8_stream(Workload(68, "f8-body-tail", "bf16", 8, 8, 128, (50, 50), 2, 2, 0, 3, None), check_steps=[2],
+                   tiles=16)
+
+
 def test_fp8_1k_shape():
     cfg = Workload(3, "1k", "bf16", 12, 12, 128, (60, 104), 3, 6, 0, 2, 25)
     run_fp8_stream(cfg, check_steps=[0, 1], tiles=32)

@@ -181,6 +181,14 @@ def test_forced_splits(splits):
     run_stream(Workload(18, "r-split-mask", "bf16", 2, 2, 64, (10, 30), 2, 4, 0, 4, 30), splits=splits)
 
 
+def test_uneven_split_every_row():
+    """A dense head_dim 128 step of 320 work items (8 heads x 40 query tiles over 40 key tiles):
+    more than half a round and less than one round of 512 resident work-groups, so the library
+    cuts every item into a body of 32 key tiles and a tail of 8 and combines the two (the 480P
+    case at a size the oracle checks on every row)."""
+    run_stream(Workload(38, "r-body-tail", "bf16", 8, 8, 128, (50, 50), 2, 2, 0, 3, None))
+
+
 @pytest.mark.parametrize("hpw", [1, 2, 4])
 def test_heads_per_workgroup(hpw):
     run_stream(Workload(19, "r-hpw", "bf16", 8, 2, 128, (10, 25), 1, 3, 0, 3, None), heads_per_wg=hpw)

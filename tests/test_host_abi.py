@@ -516,6 +516,39 @@ def test_split_rule_dense_and_masked():
         uf.uf_kvcache_destroy(h)
 
 
+@pytest.mark.skipif(_stub_launches() is None, reason="only with the host-only build (launch stubs)")
+def test_uneven_split_rule():
+    """480P shape (12 heads of 128, 30x52 tokens per frame, 3 queried frames over 3 anchor and
+    9 window frames): 444 work items, more than half a round but less than one round of 512
+    resident work-groups, so a dense step is cut into bodies of 119 key tiles and tails of the
+    other 28 (attention launch and combine).  Unsplit instead under a block mask, at head_dim 64,
+    through the static scratch (the partials do not fit) and when the split count is forced."""
+    L, H, d = 30 * 52, 12, 128
+    n_q, n_k = 3 * L, 12 * L
+    nqb, nkb = -(-n_q // 128), -(-n_k // 128)
+    assert (nqb * H, nkb) == (444, 147)
+    for kw, dd, mask, static, want in (
+            ({}, d, None, False, (2, nkb - (3 * nkb + 8) // 16)),
+            ({}, d, _mask(1, nqb, nkb), False, (1, 0)),
+            ({}, 64, None, False, (1, 0)),
+            ({}, d, None, True, (1, 0)),
+            (dict(splits=2), d, None, False, (2, 0))):
+        ws_bytes = uf.uf_attn_workspace_bytes(desc(H=H, d=dd, L=L, W=9, A=3))
+        st, h = create(H=H, d=dd, L=L, W=9, A=3, ws=FAKE * 1024, ws_bytes=ws_bytes, **kw)
+        assert st == uf.UF_OK, uf.uf_last_error()
+        try:
+            uf.uf_kvcache_append(h, None, None, 12, uf.UF_APPEND_COMMIT_ONLY, 0)
+            q, out = _tensor(n_q, H, d=dd, data=FAKE * 32), _tensor(n_q, H, d=dd, data=FAKE * 64)
+            call = LIB.uf_attn_step_static if static else LIB.uf_attn_step
+            n0 = _stub_launches()
+            got = call(ctypes.byref(q), h, ctypes.byref(mask) if mask is not None else None, ctypes.byref(out), None)
+            assert got == uf.UF_OK, uf.uf_last_error()
+            assert (LIB.uf_stub_last_splits(), LIB.uf_stub_last_split_tile()) == want, (kw, dd, static)
+            assert _stub_launches() == n0 + (2 if want[0] > 1 else 1)
+        finally:
+            uf.uf_kvcache_destroy(h)
+
+
 def test_largest_head_storage_is_accepted():
     """Just under 4 GiB of K per head (bf16) is accepted, and so are 2^24 rows of E4M3 codes
     (2 GiB), whose bf16 twin is refused."""

@@ -13,7 +13,10 @@ constexpr int kAttnTile = 128;  // keys per tile = block-mask tile = query rows 
 
 // What one lane of one work-group computes.  The grid enumerates (query block, split, head
 // group) items, dealt to XCDs in windows (xcd_windowed); a work-group covers 128 / heads_per_wg
-// queries of heads_per_wg query heads of one KV group, one 32-query row block per wave.
+// queries of heads_per_wg query heads of one KV group, one 32-query row block per wave.  With
+// an uneven two-part split (split_tile) the grid holds the long first parts of all items, then
+// the short second parts, which start on the slots that free up (work-groups are dispatched in
+// grid order as slots free up).
 struct AttnItem {
   int split;   // part of the key range
   int q_tile;  // block-mask row (query tile)
@@ -24,14 +27,23 @@ struct AttnItem {
 };
 
 __device__ inline AttnItem attn_item(const AttnParams& p, int block, int n_blocks, int wave, int l32) {
-  const int item = xcd_windowed(block, n_blocks);
+  int item, split;
+  if (p.split_tile) {
+    const int per = n_blocks / 2;
+    split = block >= per ? 1 : 0;
+    item = xcd_windowed(block - split * per, per);
+  } else {
+    const int x = xcd_windowed(block, n_blocks);
+    const int rest = x / p.n_qblk;
+    split = rest % p.splits;
+    item = x % p.n_qblk + (rest / p.splits) * p.n_qblk;
+  }
   const int qblk = item % p.n_qblk;
-  const int rest = item / p.n_qblk;
-  const int hgrp = rest / p.splits;
+  const int hgrp = item / p.n_qblk;
   const int waves_per_head = 4 / p.heads_per_wg;
   const int q0 = qblk * (kAttnTile / p.heads_per_wg);
   AttnItem it;
-  it.split = rest % p.splits;
+  it.split = split;
   it.q_tile = q0 / kAttnTile;
   it.head = hgrp * p.heads_per_wg + wave / waves_per_head;
   it.kvh = (hgrp * p.heads_per_wg) / p.group;
@@ -76,8 +88,14 @@ struct KeyTiles {
 
   __device__ KeyTiles(const AttnParams& p, const AttnItem& it) {
     const int nkt = (p.n_k + kAttnTile - 1) / kAttnTile;
-    const int lo = (int)(((int64_t)it.split * nkt) / p.splits);
-    hi = (int)(((int64_t)(it.split + 1) * nkt) / p.splits);
+    int lo;
+    if (p.split_tile) {
+      lo = it.split ? p.split_tile : 0;
+      hi = it.split ? nkt : p.split_tile;
+    } else {
+      lo = (int)(((int64_t)it.split * nkt) / p.splits);
+      hi = (int)(((int64_t)(it.split + 1) * nkt) / p.splits);
+    }
     w0 = lo - 64;
     bits = own_bits = 0;
     mrow = own_row = nullptr;

@@ -45,6 +45,8 @@ struct AttnParams {
   int32_t n_qblk;              // query blocks of 128 / heads_per_wg rows
   int32_t n_hgrp;              // n_q_heads / heads_per_wg
   int32_t splits;              // key-range splits (1 = write out directly)
+  int32_t split_tile;          // > 0: two uneven parts, key tiles [0, split_tile) and [split_tile, n_kb),
+                               // every item's first part before any second part in the grid
   int32_t anchor_keys;         // logical keys [0, anchor_keys) are storage rows [0, anchor_keys)
   int32_t ring_base;           // storage row of ring slot 0 (= A * L)
   int32_t ring_cap;            // W * L
