@@ -10,7 +10,7 @@
 
 namespace {
 int g_launches = 0;
-int g_last_splits = 0, g_last_split_tile = 0;
+int g_last_splits = 0, g_last_split_tile = 0, g_last_pipelined = -1;
 
 void require(bool ok, const char* what) {
   if (!ok) {
@@ -24,6 +24,8 @@ extern "C" int uf_stub_launch_count(void) { return g_launches; }
 // key-range parts and body tiles of the last attention launch
 extern "C" int uf_stub_last_splits(void) { return g_last_splits; }
 extern "C" int uf_stub_last_split_tile(void) { return g_last_split_tile; }
+// loop of the last bf16 attention launch (1 = software-pipelined)
+extern "C" int uf_stub_last_pipelined(void) { return g_last_pipelined; }
 
 namespace uf {
 
@@ -56,8 +58,10 @@ static void check_attn(const AttnParams& p) {
   g_last_split_tile = p.split_tile;
 }
 
-hipError_t launch_attention(const AttnParams& p, int, hipStream_t) {
+hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t) {
   check_attn(p);
+  require(p.pipelined == 0 || (p.pipelined == 1 && head_dim == 128), "attention loop");
+  g_last_pipelined = p.pipelined;
   ++g_launches;
   return hipSuccess;
 }

@@ -6,6 +6,8 @@ anchor, frames per step, KV heads and query heads per KV head, head_dim 64 or 12
 per-head or shared masks of several densities, heads per work-group and forced key-range
 splits; along the stream the window is cropped and restored and the newest chunk rewritten in
 place.  Every step's attention is compared with the oracle's on every row, to the parity bar.
+At head_dim 128 every stream also runs through the software-pipelined attention loop (forced
+through the cache description), whose output must equal the one-sub-tile loop's bit for bit.
 """
 import numpy as np
 import pytest
@@ -56,20 +58,30 @@ def test_random_stream(case):
     cfg, shared, hpw, splits = case
     L, F, W, A = cfg.tokens_per_frame, cfg.frames_per_step, cfg.window_frames, cfg.anchor_frames
     print(f"random stream {_id(case)}", flush=True)
-    cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, W, A, heads_per_wg=hpw, splits=splits)
+    # at head_dim 128 the stream runs through both attention loops: one sub-tile per step in
+    # `cache`, software-pipelined in its twin, which must agree bit for bit
+    twin_loops = cfg.head_dim == 128
+    cache = KVCache(cfg.n_kv_heads, cfg.head_dim, L, W, A, heads_per_wg=hpw, splits=splits,
+                    pipeline=1 if twin_loops else 0)
+    caches = [cache]
+    if twin_loops:
+        caches.append(KVCache(cfg.n_kv_heads, cfg.head_dim, L, W, A, heads_per_wg=hpw, splits=splits, pipeline=2))
     win = oracle.FrameListWindow(L, W, A)
     for s in range(cfg.steps):
         qb, kb, vb = draw_step_tensors(cfg, s)
-        cache.append(to_dev(kb), to_dev(vb), F)
+        for c in caches:
+            c.append(to_dev(kb), to_dev(vb), F)
         win.append(bf16_bits_to_f32(kb), bf16_bits_to_f32(vb), F)
         if s == 1:  # rewrite the newest chunk in place (a second denoising pass of the same chunk)
             kb2 = f32_to_bf16_bits(draw_normal(cfg.index, s + 50, 1, kb.shape))
             vb2 = f32_to_bf16_bits(draw_normal(cfg.index, s + 50, 2, vb.shape))
-            cache.append(to_dev(kb2), to_dev(vb2), F, uf.UF_APPEND_OVERWRITE_NEWEST)
+            for c in caches:
+                c.append(to_dev(kb2), to_dev(vb2), F, uf.UF_APPEND_OVERWRITE_NEWEST)
             win.overwrite_newest(bf16_bits_to_f32(kb2), bf16_bits_to_f32(vb2), F)
         crop = W > F and s == cfg.steps - 1
         if crop:  # the last step sees a cropped window
-            cache.set_window(F)
+            for c in caches:
+                c.set_window(F)
             win.set_active(F)
         n_k = cache.window().n_keys
         kk, vv = win.keys_values()
@@ -81,10 +93,17 @@ def test_random_stream(case):
         q = to_dev(qb)
         out = torch.empty_like(q)
         cache.attn_step(q, out, mask_d)
+        if twin_loops:
+            out2 = torch.empty_like(q)
+            caches[1].attn_step(q, out2, mask_d)
         torch.cuda.synchronize()
         ref = oracle.attend(bf16_bits_to_f32(qb), kk, vv, mask_np)
         assert_close(f32_of(out), ref, f"{cfg.name} step {s}")
+        if twin_loops:
+            assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), f"{cfg.name} step {s}: loops differ"
         if crop:
-            cache.set_window(W)
+            for c in caches:
+                c.set_window(W)
             win.set_active(W)
-    cache.close()
+    for c in caches:
+        c.close()

@@ -46,9 +46,10 @@ def test_status_strings():
 
 
 def desc(H=2, d=128, L=64, W=3, A=0, k=KS, v=VS, ws=None, ws_bytes=0, hpw=0, splits=0, max_q_heads=0,
-         max_q_tokens=0):
+         max_q_tokens=0, pipeline=0):
     dd = uf.uf_kvcache_desc(H, d, L, W, A, k, v, ws, ws_bytes)
     dd.heads_per_wg, dd.splits, dd.max_q_heads, dd.max_q_tokens = hpw, splits, max_q_heads, max_q_tokens
+    dd.pipeline = pipeline
     return dd
 
 
@@ -77,6 +78,8 @@ def create(**kw):
     (dict(splits=-1), uf.UF_ERR_INVALID_ARG),
     (dict(max_q_heads=-1), uf.UF_ERR_INVALID_ARG),
     (dict(max_q_tokens=-5), uf.UF_ERR_INVALID_ARG),
+    (dict(pipeline=3), uf.UF_ERR_INVALID_ARG),
+    (dict(pipeline=-1), uf.UF_ERR_INVALID_ARG),
 ])
 def test_create_rejects(kw, status):
     st, h = create(**kw)
@@ -545,6 +548,38 @@ def test_uneven_split_rule():
             assert got == uf.UF_OK, uf.uf_last_error()
             assert (LIB.uf_stub_last_splits(), LIB.uf_stub_last_split_tile()) == want, (kw, dd, static)
             assert _stub_launches() == n0 + (2 if want[0] > 1 else 1)
+        finally:
+            uf.uf_kvcache_destroy(h)
+
+
+@pytest.mark.skipif(_stub_launches() is None, reason="only with the host-only build (launch stubs)")
+def test_pipeline_rule():
+    """The software-pipelined loop is taken at head_dim 128 when every part of the key range spans
+    at least 16 key tiles: the 480P step (bodies of 119 and tails of 28 tiles) and a masked 2K-like
+    step take it, the decoder's three 8-tile parts do not; the descriptor forces either loop;
+    head_dim 64 never takes it."""
+    cases = (  # (H, HQ, d, L, W, A, queried frames, mask, pipeline, want)
+        (12, 12, 128, 30 * 52, 9, 3, 3, False, 0, 1),
+        (12, 12, 128, 30 * 52, 9, 3, 3, False, 1, 0),
+        (3, 12, 128, 1560, 2, 0, 1, False, 0, 0),
+        (3, 12, 128, 1560, 2, 0, 1, False, 2, 1),
+        (12, 12, 128, 90 * 156, 6, 0, 3, True, 0, 1),
+        (3, 24, 64, 45 * 80, 2, 0, 2, False, 2, 0),
+    )
+    for H, HQ, d, L, W, A, fq, masked, pipeline, want in cases:
+        ws_bytes = uf.uf_attn_workspace_bytes(desc(H=H, d=d, L=L, W=W, A=A))
+        st, h = create(H=H, d=d, L=L, W=W, A=A, ws=FAKE * 1024, ws_bytes=ws_bytes, pipeline=pipeline)
+        assert st == uf.UF_OK, uf.uf_last_error()
+        try:
+            uf.uf_kvcache_append(h, None, None, A + W, uf.UF_APPEND_COMMIT_ONLY, 0)
+            n_q, n_k = fq * L, (A + W) * L
+            # q and out 4 GiB apart, away from the fake workspace: the 2K-like step's q alone spans 129 MB
+            q, out = _tensor(n_q, HQ, d=d, data=FAKE * 4096), _tensor(n_q, HQ, d=d, data=FAKE * 8192)
+            m = _mask(HQ, -(-n_q // 128), -(-n_k // 128)) if masked else None
+            got = LIB.uf_attn_step(ctypes.byref(q), h, ctypes.byref(m) if m is not None else None,
+                                   ctypes.byref(out), None)
+            assert got == uf.UF_OK, uf.uf_last_error()
+            assert LIB.uf_stub_last_pipelined() == want, (H, HQ, d, L, pipeline)
         finally:
             uf.uf_kvcache_destroy(h)
 

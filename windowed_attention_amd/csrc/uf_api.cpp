@@ -43,6 +43,7 @@ uf_status hip_fail(hipError_t e, const char* what) {
 
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;
 constexpr int kMaxSplits = 16;
+constexpr int kPipelineMinTiles = 16;  // key tiles per part from which the pipelined loop is taken
 
 float fp8_attention_q_scale(const uf_kvcache_desc& d, int* e_out);
 
@@ -69,6 +70,8 @@ uf_status check_desc(const uf_kvcache_desc* d) {
     return fail(UF_ERR_INVALID_ARG, "heads_per_wg must be 0, 1, 2 or 4 (got %d)", d->heads_per_wg);
   if (d->splits < 0 || d->splits > kMaxSplits)
     return fail(UF_ERR_INVALID_ARG, "splits must lie in 0..%d (got %d)", kMaxSplits, d->splits);
+  if (d->pipeline < 0 || d->pipeline > 2)
+    return fail(UF_ERR_INVALID_ARG, "pipeline must be 0, 1 or 2 (got %d)", d->pipeline);
   if (d->kv_dtype != UF_BF16 && d->kv_dtype != UF_FP8_E4M3)
     return fail(UF_ERR_DTYPE, "kv_dtype must be UF_BF16 or UF_FP8_E4M3 (got %d)", d->kv_dtype);
   if (d->kv_dtype == UF_FP8_E4M3) {
@@ -538,6 +541,12 @@ uf_status attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mask* 
   p.blk_h = d.block_grid_h;
   p.blk_w = d.block_grid_w;
   p.blk_frames = cache->block_frames;
+  // The software-pipelined loop gains on long key walks (1.3-1.5% at the 480P, 1K and 2K
+  // steps) and loses on short ones (its first and last sub-tiles run without overlap: the
+  // decoder's 8-tile parts are 1.2-1.6% slower), so it is taken when every part spans at least
+  // 16 key tiles.
+  const int part_tiles = split_tile ? std::min(split_tile, n_kt - split_tile) : n_kt / splits;
+  p.pipelined = d.kv_dtype == UF_BF16 && d.head_dim == 128 && (d.pipeline == 2 || (d.pipeline == 0 && part_tiles >= kPipelineMinTiles));
   hipError_t e;
   if (d.kv_dtype == UF_FP8_E4M3) {
     uf::AttnFp8Params f;

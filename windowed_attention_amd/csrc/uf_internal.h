@@ -59,6 +59,7 @@ struct AttnParams {
   float* ws_o;                 // [splits][n_q][n_q_heads][d] unnormalised partial outputs
   float* ws_ml;                // [splits][n_q][n_q_heads][2]: running max (log2 units), sum
   int32_t blk_h, blk_w, blk_frames;  // != 0: query row i is token block_src_token(i) of q and out
+  int32_t pipelined;           // head_dim 128: 1 = the software-pipelined loop, 0 = one sub-tile per step
 };
 
 // FP8 (E4M3) cache: the same append with each value quantized, code = E4M3(x * inv_scale),

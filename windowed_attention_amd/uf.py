@@ -56,7 +56,7 @@ class uf_kvcache_desc(ctypes.Structure):
                 ("q_scale", ctypes.c_float), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
                 ("block_grid_h", ctypes.c_int32), ("block_grid_w", ctypes.c_int32),
                 ("max_q_heads", ctypes.c_int32), ("max_q_tokens", ctypes.c_int32),
-                ("heads_per_wg", ctypes.c_int32), ("splits", ctypes.c_int32)]
+                ("heads_per_wg", ctypes.c_int32), ("splits", ctypes.c_int32), ("pipeline", ctypes.c_int32)]
 
 
 class uf_block_mask(ctypes.Structure):
@@ -262,7 +262,7 @@ class KVCache:
                  anchor_frames: int = 0, device="cuda", workspace: bool = True, kv_dtype: int = UF_BF16,
                  q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0, block_grid=(0, 0),
                  max_q_heads: int = 0, max_q_tokens: int = 0, heads_per_wg: int = 0, splits: int = 0,
-                 k_storage=None, v_storage=None, workspace_bytes: int = None):
+                 k_storage=None, v_storage=None, workspace_bytes: int = None, pipeline: int = 0):
         """k_storage / v_storage: caller-made device tensors of the storage's shape
         [n_kv_heads, (anchor_frames + window_frames) * tokens_per_frame, head_dim] (bf16, or uint8
         for FP8), e.g. views into larger buffers; allocated here when not given.
@@ -270,7 +270,8 @@ class KVCache:
         import torch
         desc = uf_kvcache_desc(n_kv_heads, head_dim, tokens_per_frame, window_frames, anchor_frames,
                                None, None, None, 0, kv_dtype, q_scale, k_scale, v_scale,
-                               block_grid[0], block_grid[1], max_q_heads, max_q_tokens, heads_per_wg, splits)
+                               block_grid[0], block_grid[1], max_q_heads, max_q_tokens, heads_per_wg, splits,
+                               pipeline)
         nbytes = uf_kvcache_storage_bytes(desc)
         if nbytes == 0:
             _check(_lib.uf_kvcache_create(ctypes.byref(desc), ctypes.byref(ctypes.c_void_p())), "KVCache")
