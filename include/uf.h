@@ -162,7 +162,8 @@ typedef struct uf_kvcache_desc {
                                allow as many) */
   int32_t pipeline;         /* attention loop of a bf16 cache at head_dim 128: 0 = the library's
                                choice (software-pipelined when every part of the key range spans
-                               at least 16 key tiles), 1 = one 64-key sub-tile per step,
+                               at least 16 key tiles and the work-group's heads do not walk the
+                               union of per-head mask rows), 1 = one 64-key sub-tile per step,
                                2 = software-pipelined (the scores of the next sub-tile are
                                multiplied while the current one's probabilities are computed).
                                Both give the same results bit for bit; other caches ignore it */

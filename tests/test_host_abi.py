@@ -556,19 +556,21 @@ def test_uneven_split_rule():
 def test_pipeline_rule():
     """The software-pipelined loop is taken at head_dim 128 when every part of the key range spans
     at least 16 key tiles: the 480P step (bodies of 119 and tails of 28 tiles) and a masked 2K-like
-    step take it, the decoder's three 8-tile parts do not; the descriptor forces either loop;
-    head_dim 64 never takes it."""
-    cases = (  # (H, HQ, d, L, W, A, queried frames, mask, pipeline, want)
-        (12, 12, 128, 30 * 52, 9, 3, 3, False, 0, 1),
-        (12, 12, 128, 30 * 52, 9, 3, 3, False, 1, 0),
-        (3, 12, 128, 1560, 2, 0, 1, False, 0, 0),
-        (3, 12, 128, 1560, 2, 0, 1, False, 2, 1),
-        (12, 12, 128, 90 * 156, 6, 0, 3, True, 0, 1),
-        (3, 24, 64, 45 * 80, 2, 0, 2, False, 2, 0),
+    step take it, the decoder's three 8-tile parts do not, nor a GQA step whose work-groups walk
+    the union of per-head mask rows; the descriptor forces either loop; head_dim 64 never takes it."""
+    cases = (  # (H, HQ, d, L, W, A, queried frames, mask, heads per work-group, pipeline, want)
+        (12, 12, 128, 30 * 52, 9, 3, 3, False, 0, 0, 1),
+        (12, 12, 128, 30 * 52, 9, 3, 3, False, 0, 1, 0),
+        (3, 12, 128, 1560, 2, 0, 1, False, 0, 0, 0),
+        (3, 12, 128, 1560, 2, 0, 1, False, 0, 2, 1),
+        (12, 12, 128, 90 * 156, 6, 0, 3, True, 0, 0, 1),
+        (3, 12, 128, 90 * 156, 2, 0, 1, True, 4, 0, 0),
+        (3, 12, 128, 90 * 156, 2, 0, 1, True, 1, 0, 1),
+        (3, 24, 64, 45 * 80, 2, 0, 2, False, 0, 2, 0),
     )
-    for H, HQ, d, L, W, A, fq, masked, pipeline, want in cases:
+    for H, HQ, d, L, W, A, fq, masked, hpw, pipeline, want in cases:
         ws_bytes = uf.uf_attn_workspace_bytes(desc(H=H, d=d, L=L, W=W, A=A))
-        st, h = create(H=H, d=d, L=L, W=W, A=A, ws=FAKE * 1024, ws_bytes=ws_bytes, pipeline=pipeline)
+        st, h = create(H=H, d=d, L=L, W=W, A=A, ws=FAKE * 1024, ws_bytes=ws_bytes, hpw=hpw, pipeline=pipeline)
         assert st == uf.UF_OK, uf.uf_last_error()
         try:
             uf.uf_kvcache_append(h, None, None, A + W, uf.UF_APPEND_COMMIT_ONLY, 0)

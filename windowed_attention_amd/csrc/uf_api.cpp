@@ -544,9 +544,13 @@ uf_status attn_step(const uf_tensor* q, uf_kvcache* cache, const uf_block_mask* 
   // The software-pipelined loop gains on long key walks (1.3-1.5% at the 480P, 1K and 2K
   // steps) and loses on short ones (its first and last sub-tiles run without overlap: the
   // decoder's 8-tile parts are 1.2-1.6% slower), so it is taken when every part spans at least
-  // 16 key tiles.
+  // 16 key tiles.  A union walk (per-head masks shared by a work-group's heads) keeps the
+  // one-sub-tile loop, which skips the tiles a wave's head does not keep instead of computing
+  // them at -inf.
   const int part_tiles = split_tile ? std::min(split_tile, n_kt - split_tile) : n_kt / splits;
-  p.pipelined = d.kv_dtype == UF_BF16 && d.head_dim == 128 && (d.pipeline == 2 || (d.pipeline == 0 && part_tiles >= kPipelineMinTiles));
+  const bool union_walk = per_head_mask && hpw > 1;
+  p.pipelined = d.kv_dtype == UF_BF16 && d.head_dim == 128 &&
+                (d.pipeline == 2 || (d.pipeline == 0 && part_tiles >= kPipelineMinTiles && !union_walk));
   hipError_t e;
   if (d.kv_dtype == UF_FP8_E4M3) {
     uf::AttnFp8Params f;
