@@ -42,7 +42,7 @@ constexpr int kAttnTileKeys = 128;  // keys per tile = block-mask tile
 //   * one sub-tile per step: S, softmax and P.V of sub-tile j, then a barrier;
 //   * software-pipelined (head_dim 128, long key walks): step j multiplies S of
 //     sub-tile j + 1 while it exponentiates the scores of sub-tile j, then
-//     P.V of sub-tile j while it takes the maximum of the new scores, so that
+//     P.V of sub-tile j, then takes the maximum of the new scores, so that
 //     each wave has exponentials to issue beside both of its MFMA blocks.  K
 //     is copied two sub-tiles ahead and V one ahead, in the same 64 KB.
 // Both take the same arithmetic in the same order, so their outputs are
@@ -319,7 +319,7 @@ __global__ void __launch_bounds__(kAttnThreads, attn_wgs_per_cu<D>()) attn_kerne
   } else {
     // ---- software-pipelined loop.  Sub-tile j has K in buffer pair j % 2 and V in the same pair.
     // Iteration j multiplies S of sub-tile j + 1 while it exponentiates the scores of sub-tile j,
-    // then P.V of sub-tile j while it takes the maximum of the new scores.  K is copied two
+    // then P.V of sub-tile j, then takes the maximum of the new scores.  K is copied two
     // sub-tiles ahead, V one ahead: during iteration j the copies write K of j + 2 into pair j % 2
     // (its K was last read in iteration j - 1) and V of j + 1 into pair (j + 1) % 2 (its V was last
     // read in iteration j - 1).
@@ -339,9 +339,9 @@ __global__ void __launch_bounds__(kAttnThreads, attn_wgs_per_cu<D>()) attn_kerne
       return n;
     };
     auto kbuf = [&](int j) -> char* { return smem + (j & 1) * 2 * SUB_B; };
-    // the scores of sub-tile s, whose K sits at kb; copies (K with offsets ck into kd, V with cv into vd)
-    // go out one per d chunk
-    auto scores = [&](const char* kb, const Sub& s, f32x16 (&sc)[2], const uint32_t (&ck)[NLD], char* kd,
+    // the scores of the sub-tile whose K sits at kb; copies (K with offsets ck into kd, V with cv
+    // into vd) go out one per d chunk
+    auto scores = [&](const char* kb, f32x16 (&sc)[2], const uint32_t (&ck)[NLD], char* kd,
                       const uint32_t (&cv)[NLD], char* vd) {
       sc[0] = f32x16{};
       sc[1] = f32x16{};
@@ -442,6 +442,8 @@ __global__ void __launch_bounds__(kAttnThreads, attn_wgs_per_cu<D>()) attn_kerne
       pv_pair(tb, pb, 0, va);
       pv_pair(tb, pb, 2, va);
     };
+    // the reference point in log2 units; 0 while this wave has seen no visible key (every score so
+    // far -inf), so that the probabilities of an unkept sub-tile come out 0 instead of NaN
     auto ref_of = [&]() { return m_run == -INFINITY ? 0.f : m_run * c2; };
 
     Sub s0;
@@ -467,7 +469,7 @@ __global__ void __launch_bounds__(kAttnThreads, attn_wgs_per_cu<D>()) attn_kerne
     if (s0.kt >= 0) {
       // scores of sub-tile 0; the copies that go out with them write K and V of sub-tile 1 into
       // pair 1, which nothing reads before the barrier below (K is the same data again)
-      scores(kbuf(0), s0, sa, ko1, kbuf(1), ko1, kbuf(1) + SUB_B);
+      scores(kbuf(0), sa, ko1, kbuf(1), ko1, kbuf(1) + SUB_B);
       mask_scores(s0, sa);
       update_ref(row_max(sa));
     }
@@ -480,7 +482,7 @@ __global__ void __launch_bounds__(kAttnThreads, attn_wgs_per_cu<D>()) attn_kerne
       const float mc = ref_of();
       bf16x8 pb[4];
       float lsum = l_run;
-      scores(kbuf(j + 1), s1, nxt, ko2, kbuf(j), ko1, kbuf(j + 1) + SUB_B);
+      scores(kbuf(j + 1), nxt, ko2, kbuf(j), ko1, kbuf(j + 1) + SUB_B);
       probs(cur, 0, mc, pb, lsum);
       bf16x8 va[2][ND];
 #pragma unroll
