@@ -76,15 +76,16 @@ def test_captured_step_replays_bit_exact(kind):
     cache.close()
 
 
-@pytest.mark.parametrize("entry", ["attn_step", "attn_step_static"])
-def test_captured_split_step_merges_on_every_replay(entry):
+@pytest.mark.parametrize("entry,pipeline", [("attn_step", 0), ("attn_step_static", 0), ("attn_step", 2)])
+def test_captured_split_step_merges_on_every_replay(entry, pipeline):
     """A step whose key range is split (attention parts, then the combine kernel) captured as
     the cache's first step, replayed with eager split steps in between, through the workspace
-    and through the static scratch.  Every replay and every eager step must equal the eager
+    and through the static scratch, and with the head_dim 128 kernel's software-pipelined loop.  Every replay and every eager step must equal the eager
     result of a twin cache bit for bit."""
     cfg = Workload(51, "g-split", "bf16", 8, 2, 128, (12, 25), 1, 3, 0, 4, None)
     F = cfg.frames_per_step
-    mk = lambda: KVCache(cfg.n_kv_heads, cfg.head_dim, cfg.tokens_per_frame, cfg.window_frames, 0, splits=3)
+    mk = lambda: KVCache(cfg.n_kv_heads, cfg.head_dim, cfg.tokens_per_frame, cfg.window_frames, 0, splits=3,
+                         pipeline=pipeline)
     cache, twin = mk(), mk()
     dev = [tuple(to_dev(x) for x in draw_step_tensors(cfg, s)) for s in range(cfg.steps)]
     for s in range(cfg.steps):

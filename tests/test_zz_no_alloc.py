@@ -52,15 +52,17 @@ def _compare(cfg, bare, full, win, qb, n_q, mask_pct, what):
     assert_close(f32_of(a), ref, what)
 
 
-@pytest.mark.parametrize("splits", [0, 3])
-def test_static_scratch_matches_workspace(splits):
+@pytest.mark.parametrize("splits,pipeline", [(0, 0), (3, 0), (3, 2)])
+def test_static_scratch_matches_workspace(splits, pipeline):
     # 12 query heads over 3 KV heads, 1200 queries over 3600 keys: few enough work items that
-    # the library splits the key range (forced to 3 parts in the second case)
+    # the library splits the key range (forced to 3 parts in the other cases; in the last one
+    # the head_dim 128 kernel also takes its software-pipelined loop)
     cfg = Workload(80, "no-alloc", "bf16", 12, 3, 128, (30, 40), 1, 3, 0, 3, None)
-    bare, full, win, qb = _stream(cfg, 3, splits=splits)
-    _compare(cfg, bare, full, win, qb, 1200, None, f"splits {splits or 'auto'}, first call")
+    bare, full, win, qb = _stream(cfg, 3, splits=splits, pipeline=pipeline)
+    what = f"splits {splits or 'auto'}{', pipelined loop' if pipeline == 2 else ''}"
+    _compare(cfg, bare, full, win, qb, 1200, None, f"{what}, first call")
     # the second call is smaller: fewer queries, a per-head mask
-    _compare(cfg, bare, full, win, qb, 300, 60, f"splits {splits or 'auto'}, second call, smaller")
+    _compare(cfg, bare, full, win, qb, 300, 60, f"{what}, second call, smaller")
     bare.close()
     full.close()
 
